@@ -1,0 +1,229 @@
+"""NABLA block-sparse attention for MI355X (gfx950): Python binding of libnabla.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libnabla.so``, called through its C ABI (``include/nabla.h``). PyTorch is used
+for device memory and the current HIP stream. There is no CPU fallback: if the
+library is not built, every call raises.
+
+Entry points (same names as the C ABI):
+    nabla_build_mask(q, k, thr, sta=None, ...)      -> dict of block lists
+    nabla_sparse_attn_fwd(q, k, v, kv_count, kv_idx) -> (o, lse)
+    nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx)
+                                                     -> (dq, dk, dv)
+    nabla_workspace_size(op, B, H, S, D, N), nabla_status_string(code)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnabla.so")
+
+NABLA_OK = 0
+NABLA_OP_MASK, NABLA_OP_FWD, NABLA_OP_BWD = 0, 1, 2
+BLOCK_N = 64
+
+EXPORTED_SYMBOLS = (
+    "nabla_workspace_size",
+    "nabla_status_string",
+    "nabla_build_mask",
+    "nabla_sparse_attn_fwd",
+    "nabla_sparse_attn_bwd",
+)
+
+
+class NablaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {nabla_status_string(status)} ({status})")
+
+
+class StaWindow(ctypes.Structure):
+    """nabla_sta_t: latent grid T x Hs x Ws, tile edge P, window in tokens."""
+    _fields_ = [(name, ctypes.c_int32) for name in ("T", "Hs", "Ws", "P", "win_t", "win_h", "win_w")]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libnabla.so (built by ``python -m block_sparse_attention_nabla_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m block_sparse_attention_nabla_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.nabla_workspace_size.restype = ctypes.c_size_t
+    lib.nabla_workspace_size.argtypes = [_i32] * 6
+    lib.nabla_status_string.restype = ctypes.c_char_p
+    lib.nabla_status_string.argtypes = [ctypes.c_int]
+    lib.nabla_build_mask.restype = ctypes.c_int
+    lib.nabla_build_mask.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                     ctypes.POINTER(StaWindow), _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]
+    lib.nabla_sparse_attn_fwd.restype = ctypes.c_int
+    lib.nabla_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                          ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.nabla_sparse_attn_bwd.restype = ctypes.c_int
+    lib.nabla_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                          _i32, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                          _vp, ctypes.c_size_t, _vp]
+    _lib = lib
+    return lib
+
+
+def nabla_status_string(status: int) -> str:
+    return load_library().nabla_status_string(int(status)).decode()
+
+
+def nabla_workspace_size(op: int, B: int, H: int, S: int, D: int, N: int = BLOCK_N) -> int:
+    return int(load_library().nabla_workspace_size(op, B, H, S, D, N))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_qkv(name: str, t: torch.Tensor, shape=None):
+    if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, S, D]")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _workspace(op, B, H, S, D, N, device, workspace):
+    size = nabla_workspace_size(op, B, H, S, D, N)
+    if workspace is None:
+        workspace = torch.empty(max(size, 1), dtype=torch.uint8, device=device)
+    return workspace, size
+
+
+def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, sta: Optional[dict] = None,
+                     N: int = BLOCK_N, *, transpose: bool = False, dense: bool = False,
+                     out: Optional[Dict[str, torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """Block mask of section 3.1.2 (Algorithm 1) [+ STA union of section 3.1.3] as lists.
+
+    Returns kv_count [B,H,n], kv_idx [B,H,n,n] and, if requested, q_count / q_idx
+    (``transpose``) and dense_mask uint8 [B,H,n,n] (``dense``). ``sta`` holds
+    T, Hs, Ws, P, win_t, win_h, win_w.
+    """
+    _check_qkv("q", q)
+    B, H, S, D = q.shape
+    _check_qkv("k", k, q.shape)
+    n = S // N
+    dev = q.device
+    out = dict(out or {})
+    kv_count = out.get("kv_count")
+    if kv_count is None:
+        kv_count = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    kv_idx = out.get("kv_idx")
+    if kv_idx is None:
+        kv_idx = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
+    res = {"kv_count": kv_count, "kv_idx": kv_idx}
+    q_count = q_idx = dmask = None
+    if transpose:
+        q_count = out.get("q_count")
+        q_count = torch.empty((B, H, n), dtype=torch.int32, device=dev) if q_count is None else q_count
+        q_idx = out.get("q_idx")
+        q_idx = torch.empty((B, H, n, n), dtype=torch.int32, device=dev) if q_idx is None else q_idx
+        res.update(q_count=q_count, q_idx=q_idx)
+    if dense:
+        dmask = out.get("dense_mask")
+        dmask = torch.empty((B, H, n, n), dtype=torch.uint8, device=dev) if dmask is None else dmask
+        res["dense_mask"] = dmask
+    ws, size = _workspace(NABLA_OP_MASK, B, H, S, D, N, dev, workspace)
+    sta_ptr = None
+    if sta is not None:
+        sta_ptr = ctypes.pointer(StaWindow(*(int(sta[f]) for f in ("T", "Hs", "Ws", "P", "win_t", "win_h", "win_w"))))
+    st = load_library().nabla_build_mask(
+        _ptr(q), _ptr(k), B, H, S, D, N, float(thr), sta_ptr, _ptr(kv_count), _ptr(kv_idx),
+        _ptr(q_count), _ptr(q_idx), _ptr(dmask), _ptr(ws), ws.numel(), _stream(q, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, "nabla_build_mask")
+    return res
+
+
+def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          kv_count: torch.Tensor, kv_idx: torch.Tensor,
+                          softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
+                          o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          want_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Block-sparse attention forward (eq. (4) on the kept blocks). Returns (O bf16, LSE fp32)."""
+    _check_qkv("q", q)
+    B, H, S, D = q.shape
+    _check_qkv("k", k, q.shape)
+    _check_qkv("v", v, q.shape)
+    n = S // N
+    if kv_count.dtype != torch.int32 or kv_idx.dtype != torch.int32:
+        raise ValueError("kv_count / kv_idx must be int32")
+    if tuple(kv_count.shape) != (B, H, n) or tuple(kv_idx.shape) != (B, H, n, n):
+        raise ValueError("kv_count / kv_idx shapes do not match q")
+    if not (kv_count.is_contiguous() and kv_idx.is_contiguous()):
+        raise ValueError("kv_count / kv_idx must be contiguous")
+    scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    ws, size = _workspace(NABLA_OP_FWD, B, H, S, D, N, q.device, workspace)
+    st = load_library().nabla_sparse_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), B, H, S, D, N, _ptr(kv_count), _ptr(kv_idx), scale, _ptr(o),
+        _ptr(lse) if want_lse else None, _ptr(ws), ws.numel(), _stream(q, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, "nabla_sparse_attn_fwd")
+    return o, (lse if want_lse else None)
+
+
+def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx,
+                          softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
+                          dq=None, dk=None, dv=None, workspace=None,
+                          stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Block-sparse attention backward with the mask held constant. Returns (dQ, dK, dV) bf16."""
+    _check_qkv("q", q)
+    B, H, S, D = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+        _check_qkv(name, t, q.shape)
+    n = S // N
+    for name, t, shp in (("kv_count", kv_count, (B, H, n)), ("kv_idx", kv_idx, (B, H, n, n)),
+                         ("q_count", q_count, (B, H, n)), ("q_idx", q_idx, (B, H, n, n))):
+        if t.dtype != torch.int32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor of shape {shp}")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, S]")
+    scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    ws, size = _workspace(NABLA_OP_BWD, B, H, S, D, N, q.device, workspace)
+    st = load_library().nabla_sparse_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), B, H, S, D, N, _ptr(kv_count),
+        _ptr(kv_idx), _ptr(q_count), _ptr(q_idx), scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+        ws.numel(), _stream(q, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, "nabla_sparse_attn_bwd")
+    return dq, dk, dv
+
+
+__all__ = [
+    "LIB_PATH", "BLOCK_N", "EXPORTED_SYMBOLS", "NablaError", "StaWindow", "load_library",
+    "nabla_status_string", "nabla_workspace_size", "nabla_build_mask", "nabla_sparse_attn_fwd",
+    "nabla_sparse_attn_bwd", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD",
+]

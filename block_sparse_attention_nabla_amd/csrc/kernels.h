@@ -1,0 +1,50 @@
+// kernels.h -- launchers of the gfx950 NABLA kernels (host side, after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nabla.h"
+
+namespace nabla {
+
+// STA window in tile units (one tile = one block): grid tT x tH x tW tiles,
+// window wt x wh x ww tiles. on == 0 disables the union.
+struct StaParams {
+    int on;
+    int tT, tH, tW;
+    int wt, wh, ww;
+};
+
+hipError_t launch_pool(const void* q, const void* k, float* qa, float* ka, int64_t nblocks, int D,
+                       hipStream_t stream);
+hipError_t launch_logits(const float* qa, const float* ka, float* logits, int64_t BH, int n, int D,
+                         float scale, hipStream_t stream);
+hipError_t launch_select(const float* logits, int64_t BH, int n, int keep_all, uint64_t thr_fixed,
+                         const StaParams& sta, int32_t* kv_count, int32_t* kv_idx,
+                         uint8_t* dense_mask, uint32_t* bits, int words_per_row,
+                         hipStream_t stream);
+hipError_t launch_transpose(const uint32_t* bits, int64_t BH, int n, int words_per_row,
+                            int32_t* q_count, int32_t* q_idx, hipStream_t stream);
+
+// Longest-first work order: order[0 .. BH*n) = item ids (bh*n + i) sorted by
+// counts[item] descending (ties in any order).
+hipError_t launch_lpt_order(const int32_t* counts, int64_t items, int n, int32_t* order,
+                            hipStream_t stream);
+
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t BH, int S, int D,
+                           const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                           float softmax_scale, void* o, float* lse, hipStream_t stream);
+
+hipError_t launch_bwd_delta(const void* o, const void* d_o, int64_t rows, int D, float* delta,
+                            hipStream_t stream);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_o,
+                           const float* lse, const float* delta, int64_t BH, int S, int D,
+                           const int32_t* q_count, const int32_t* q_idx, const int32_t* order,
+                           float softmax_scale, void* dk, void* dv, hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* d_o,
+                         const float* lse, const float* delta, int64_t BH, int S, int D,
+                         const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                         float softmax_scale, void* dq, hipStream_t stream);
+
+}  // namespace nabla

@@ -1,0 +1,351 @@
+// mask_kernels.hip -- the NABLA block-mask stage on gfx950.
+//
+// "NABLA: Neighborhood Adaptive Block-Level Attention", section 3.1.2,
+// Algorithm 1 (pooling, reduced softmax, CDF binarisation) and section 3.1.3
+// (union with the sliding-tile mask), followed by compaction of each mask row
+// into an ascending list of kept key blocks.
+//
+//   pool_kernel      steps 2-5: block means of Q and K (HBM streaming, fp32 sums)
+//   logits_kernel    steps 6-7 (logits part): Q_a K_a^T * scale per head, fp32 MFMA
+//   select_kernel    steps 7-11: row softmax, sort-free CDF selection by radix
+//                    select over the fp32 bit patterns of the probabilities,
+//                    STA union, ascending compaction, optional dense/bit rows
+//   transpose_kernel the key-block -> query-block lists the backward pass uses
+
+#include "common.h"
+#include "kernels.h"
+
+namespace nabla {
+
+// ---------------------------------------------------------------------------
+// Pooling: out[bh][i][d] = (1/N) * sum_{r<N} x[bh][i*N + r][d].
+// One workgroup per (block, tensor); 256 threads stream the 64 x D bf16 block
+// with 16-byte loads, sum per column in fp32, then reduce the partial rows in
+// LDS in a fixed order (deterministic).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ k,
+                                                   float* __restrict__ qa,
+                                                   float* __restrict__ ka) {
+    constexpr int CG = D / 8;           // 16-byte column groups per row
+    constexpr int RPT = 256 / CG;       // rows covered per pass
+    constexpr int PASSES = kBlockN / RPT;
+    __shared__ float part[RPT][D];
+
+    const int64_t blk = blockIdx.x;     // flattened bh * n + i
+    const uint16_t* src = (blockIdx.y == 0 ? q : k) + blk * (int64_t)kBlockN * D;
+    float* dst = (blockIdx.y == 0 ? qa : ka) + blk * D;
+
+    const int t = threadIdx.x;
+    const int cg = t % CG, r0 = t / CG;
+    uint4 raw[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+        raw[p] = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + p * RPT) * D + cg * 8);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += bf16_bits_to_f32(w[e] & 0xffffu);
+            acc[2 * e + 1] += bf16_bits_to_f32(w[e] >> 16);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[r0][cg * 8 + e] = acc[e];
+    __syncthreads();
+    if (t < D) {
+        float s = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < RPT; ++r) s += part[r][t];
+        dst[t] = s * (1.0f / kBlockN);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reduced logits: L[bh][i][j] = scale * sum_d Q_a[bh][i][d] * K_a[bh][j][d].
+// Workgroup = 4 waves = a 64 x 64 tile of (i, j); each wave one 32 x 32 tile
+// built from v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate). Each lane
+// feeds the MFMAs from one float4 of Q_a and one of K_a per 8 values of d:
+// lane-half h and component m stand for d = d0 + 4h + m on both operands.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ qa,
+                                                     const float* __restrict__ ka,
+                                                     float* __restrict__ logits, int n,
+                                                     float scale) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = lane >> 5, c = lane & 31;
+    const int64_t bh = blockIdx.z;
+    const int i0 = blockIdx.x * 64 + 32 * (wave >> 1);
+    const int j0 = blockIdx.y * 64 + 32 * (wave & 1);
+    if (i0 >= n || j0 >= n) return;  // whole-wave exit; no barriers below
+    const int qi = i0 + c, kj = j0 + c;
+    const float* qrow = qa + (bh * n + (qi < n ? qi : 0)) * D;
+    const float* krow = ka + (bh * n + (kj < n ? kj : 0)) * D;
+    const bool qok = qi < n, kok = kj < n;
+
+    f32x16_t acc = zero16();
+#pragma unroll 4
+    for (int d0 = 0; d0 < D; d0 += 8) {
+        float4 a = qok ? *reinterpret_cast<const float4*>(qrow + d0 + 4 * h) : make_float4(0, 0, 0, 0);
+        float4 b = kok ? *reinterpret_cast<const float4*>(krow + d0 + 4 * h) : make_float4(0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
+    }
+    // C layout: this lane holds column j = j0 + c and rows i = i0 + c_row(r, h).
+    if (kok) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = i0 + c_row(r, h);
+            if (i < n) logits[(bh * n + i) * (int64_t)n + kj] = acc[r] * scale;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block reductions over a 256-thread workgroup (fixed order => deterministic).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// STA window membership of key block j for query block i (clipped centred window).
+__device__ __forceinline__ bool sta_contains(const StaParams& s, int i, int j) {
+    const int ti = i / (s.tH * s.tW), yi = (i / s.tW) % s.tH, xi = i % s.tW;
+    const int tj = j / (s.tH * s.tW), yj = (j / s.tW) % s.tH, xj = j % s.tW;
+    const bool in_t = tj >= ti - (s.wt - 1) / 2 && tj <= ti + s.wt / 2;
+    const bool in_h = yj >= yi - (s.wh - 1) / 2 && yj <= yi + s.wh / 2;
+    const bool in_w = xj >= xi - (s.ww - 1) / 2 && xj <= xi + s.ww / 2;
+    return in_t && in_h && in_w;  // clipping is implicit: j is always on the grid
+}
+
+// ---------------------------------------------------------------------------
+// Selection + compaction: one workgroup (256 threads) per query block row.
+//
+// p_j = exp(L_j - max) / sum is computed in fp32. The kept set is
+// {j : G_j <= thr} with G_j = mass of entries strictly larger than p_j; it is
+// exactly {j : p_j >= tau} for the smallest probability value tau whose
+// strictly-larger mass is <= thr. tau is found MSB-first over the uint32 bit
+// patterns of the (non-negative) p_j, 8 bits per pass: a 256-bin histogram of
+// (count, mass) over the entries matching the prefix so far, a suffix sum over
+// bins, and the lowest non-empty bin whose mass-above stays <= thr. Masses are
+// summed as 2^-40 fixed-point integers, so the sums are exact and independent
+// of the order the atomics land in.
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 256;
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* __restrict__ logits, int n, int keep_all, uint64_t thr_fixed, StaParams sta,
+    int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_idx,
+    uint8_t* __restrict__ dense_mask, uint32_t* __restrict__ bits, int words_per_row) {
+    __shared__ float pv[NABLA_MAX_BLOCKS];
+    __shared__ unsigned long long hmass[256];
+    __shared__ int hcnt[256];
+    __shared__ unsigned long long wsum[4];
+    __shared__ float wred[4];
+    __shared__ int sel_bin;
+    __shared__ unsigned long long sel_above;
+    __shared__ int wcount[4];
+
+    const int64_t row = blockIdx.x;  // flattened bh * n + i
+    const int i = (int)(row % n);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const float* L = logits + row * (int64_t)n;
+
+    // 1. load the row, row maximum
+    float mx = -INFINITY;
+    for (int j = t; j < n; j += kSelThreads) {
+        const float x = L[j];
+        pv[j] = x;
+        mx = fmaxf(mx, x);
+    }
+    mx = wave_max(mx);
+    if (lane == 0) wred[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+    __syncthreads();
+
+    // 2. exponentials and their sum (fixed order per thread, then fixed tree)
+    float z = 0.f;
+    for (int j = t; j < n; j += kSelThreads) {
+        const float e = expf(pv[j] - mx);
+        pv[j] = e;
+        z += e;
+    }
+    z = wave_sum(z);
+    if (lane == 0) wred[wave] = z;
+    __syncthreads();
+    z = (wred[0] + wred[1]) + (wred[2] + wred[3]);
+    for (int j = t; j < n; j += kSelThreads) pv[j] = pv[j] / z;
+    __syncthreads();
+
+    // 3. radix select of tau over the bit patterns of p
+    uint32_t prefix = 0, pmask = 0;
+    unsigned long long above = 0;  // fixed-point mass strictly above the current prefix range
+    if (!keep_all) {
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            hmass[t] = 0ull;
+            hcnt[t] = 0;
+            __syncthreads();
+            for (int j = t; j < n; j += kSelThreads) {
+                const float p = pv[j];
+                const uint32_t key = __float_as_uint(p);
+                if ((key & pmask) == prefix) {
+                    const int d = (key >> shift) & 255;
+                    atomicAdd(&hmass[d], (unsigned long long)__float2ull_rn(p * 0x1p40f));
+                    atomicAdd(&hcnt[d], 1);
+                }
+            }
+            __syncthreads();
+            // Suffix sum over bins: bin t needs the mass of bins > t. Each
+            // thread owns bin t; inclusive suffix scan within the wave over
+            // lanes (higher lane = higher bin), then add the higher waves.
+            unsigned long long m = hmass[t];
+            unsigned long long incl = m;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned long long o = __shfl_down(incl, off);
+                if (lane + off < 64) incl += o;
+            }
+            if (lane == 0) wsum[wave] = incl;  // total of this wave's 64 bins
+            if (t == 0) sel_bin = 256;
+            __syncthreads();
+            unsigned long long higher = 0;
+            for (int w = wave + 1; w < 4; ++w) higher += wsum[w];
+            const unsigned long long mass_above_bin = above + higher + (incl - m);
+            if (hcnt[t] > 0 && mass_above_bin <= thr_fixed) atomicMin(&sel_bin, t);
+            __syncthreads();
+            const int b = sel_bin;  // always < 256: the highest non-empty bin qualifies
+            if (t == b) sel_above = mass_above_bin;
+            __syncthreads();
+            above = sel_above;
+            prefix |= (uint32_t)b << shift;
+            pmask |= 0xffu << shift;
+            __syncthreads();
+        }
+    }
+    const uint32_t tau = prefix;
+
+    // 4. decisions, STA union, ascending compaction
+    int32_t* out_idx = kv_idx + row * (int64_t)n;
+    int running = 0;
+    for (int base = 0; base < n; base += kSelThreads) {
+        const int j = base + t;
+        bool keep = false;
+        if (j < n) {
+            keep = keep_all || __float_as_uint(pv[j]) >= tau;
+            if (!keep && sta.on) keep = sta_contains(sta, i, j);
+        }
+        const unsigned long long bal = __ballot(keep);
+        const int before = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wcount[wave] = __popcll(bal);
+        __syncthreads();
+        int off = running;
+        for (int w = 0; w < wave; ++w) off += wcount[w];
+        if (keep) out_idx[off + before] = j;
+        if (dense_mask && j < n) dense_mask[row * (int64_t)n + j] = keep ? 1 : 0;
+        if (bits && lane < 2) {
+            const int word = (base + 64 * wave) / 32 + lane;
+            if (word < words_per_row)
+                bits[row * (int64_t)words_per_row + word] = (uint32_t)(bal >> (32 * lane));
+        }
+        running += wcount[0] + wcount[1] + wcount[2] + wcount[3];
+        __syncthreads();
+    }
+    if (t == 0) kv_count[row] = running;
+}
+
+// ---------------------------------------------------------------------------
+// Transpose of the kept-block relation: for key block j, the ascending list of
+// query blocks i that keep it. Workgroup = one 32-column word of the row
+// bitmasks; each wave owns 8 of those columns and walks the rows 64 at a time,
+// compacting with a ballot (no atomics, deterministic, ascending).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose_kernel(const uint32_t* __restrict__ bits, int n,
+                                                        int words_per_row,
+                                                        int32_t* __restrict__ q_count,
+                                                        int32_t* __restrict__ q_idx) {
+    const int wc = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int running[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) running[b] = 0;
+    const uint32_t* col = bits + bh * (int64_t)n * words_per_row + wc;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const uint32_t word = i < n ? col[(int64_t)i * words_per_row] : 0u;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int j = 32 * wc + 8 * wave + b;
+            const bool f = (word >> (8 * wave + b)) & 1u;
+            const unsigned long long bal = __ballot(f);
+            if (j < n && f)
+                q_idx[(bh * n + j) * (int64_t)n + running[b] + __popcll(bal & ((1ull << lane) - 1ull))] = i;
+            running[b] += __popcll(bal);
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int j = 32 * wc + 8 * wave + b;
+            if (j < n) q_count[bh * n + j] = running[b];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (called by the C ABI after validation).
+// ---------------------------------------------------------------------------
+hipError_t launch_pool(const void* q, const void* k, float* qa, float* ka, int64_t nblocks, int D,
+                       hipStream_t stream) {
+    dim3 grid((unsigned)nblocks, 2);
+    if (D == 128)
+        pool_kernel<128><<<grid, 256, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k, qa, ka);
+    else
+        pool_kernel<64><<<grid, 256, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k, qa, ka);
+    return hipGetLastError();
+}
+
+hipError_t launch_logits(const float* qa, const float* ka, float* logits, int64_t BH, int n, int D,
+                         float scale, hipStream_t stream) {
+    dim3 grid((n + 63) / 64, (n + 63) / 64, (unsigned)BH);
+    if (D == 128)
+        logits_kernel<128><<<grid, 256, 0, stream>>>(qa, ka, logits, n, scale);
+    else
+        logits_kernel<64><<<grid, 256, 0, stream>>>(qa, ka, logits, n, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const float* logits, int64_t BH, int n, int keep_all, uint64_t thr_fixed,
+                         const StaParams& sta, int32_t* kv_count, int32_t* kv_idx,
+                         uint8_t* dense_mask, uint32_t* bits, int words_per_row,
+                         hipStream_t stream) {
+    select_kernel<<<(unsigned)(BH * n), kSelThreads, 0, stream>>>(
+        logits, n, keep_all, thr_fixed, sta, kv_count, kv_idx, dense_mask, bits, words_per_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint32_t* bits, int64_t BH, int n, int words_per_row,
+                            int32_t* q_count, int32_t* q_idx, hipStream_t stream) {
+    dim3 grid((unsigned)words_per_row, (unsigned)BH);
+    transpose_kernel<<<grid, 256, 0, stream>>>(bits, n, words_per_row, q_count, q_idx);
+    return hipGetLastError();
+}
+
+}  // namespace nabla

@@ -1,0 +1,149 @@
+// nabla_api.cpp -- the extern "C" entry points declared in include/nabla.h.
+// Validate, carve the caller's workspace, enqueue the kernels on the caller's
+// stream. No allocation, no synchronisation, no state.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "kernels.h"
+#include "validate.h"
+
+using namespace nabla;
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+#define NABLA_LAUNCH(expr)                          \
+    do {                                            \
+        if ((expr) != hipSuccess) return NABLA_ERR_HIP; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* nabla_status_string(nabla_status_t status) {
+    switch (status) {
+        case NABLA_OK: return "NABLA_OK";
+        case NABLA_ERR_INVALID_ARG: return "NABLA_ERR_INVALID_ARG";
+        case NABLA_ERR_UNSUPPORTED: return "NABLA_ERR_UNSUPPORTED";
+        case NABLA_ERR_WORKSPACE: return "NABLA_ERR_WORKSPACE";
+        case NABLA_ERR_HIP: return "NABLA_ERR_HIP";
+    }
+    return "NABLA_ERR_UNKNOWN";
+}
+
+size_t nabla_workspace_size(int32_t op, int32_t B, int32_t H, int32_t S, int32_t D, int32_t N) {
+    Shape s;
+    if (check_shape(B, H, S, D, N, &s) != NABLA_OK) return 0;
+    switch (op) {
+        case NABLA_OP_MASK: return mask_workspace(s).total;
+        case NABLA_OP_FWD: return fwd_workspace(s).total;
+        case NABLA_OP_BWD: return bwd_workspace(s).total;
+    }
+    return 0;
+}
+
+nabla_status_t nabla_build_mask(const void* q, const void* k, int32_t B, int32_t H, int32_t S,
+                                int32_t D, int32_t N, float thr, const nabla_sta_t* sta,
+                                int32_t* kv_count, int32_t* kv_idx, int32_t* q_count,
+                                int32_t* q_idx, uint8_t* dense_mask, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    Shape s;
+    nabla_status_t st = check_shape(B, H, S, D, N, &s);
+    if (st != NABLA_OK) return st;
+    if (!q || !k || !kv_count || !kv_idx) return NABLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k)) return NABLA_ERR_INVALID_ARG;
+    if ((q_count == nullptr) != (q_idx == nullptr)) return NABLA_ERR_INVALID_ARG;
+    if (!(thr >= 0.0f) || isinf(thr)) return NABLA_ERR_INVALID_ARG;  // rejects NaN too
+    st = check_sta(sta, s);
+    if (st != NABLA_OK) return st;
+    const MaskWorkspace w = mask_workspace(s);
+    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
+
+    StaParams sp{};
+    if (sta) {
+        sp.on = 1;
+        sp.tT = sta->T;
+        sp.tH = sta->Hs / sta->P;
+        sp.tW = sta->Ws / sta->P;
+        sp.wt = sta->win_t;
+        sp.wh = sta->win_h / sta->P;
+        sp.ww = sta->win_w / sta->P;
+    }
+    float* qa = reinterpret_cast<float*>(ws_at(workspace, w.qa));
+    float* ka = reinterpret_cast<float*>(ws_at(workspace, w.ka));
+    float* logits = reinterpret_cast<float*>(ws_at(workspace, w.logits));
+    uint32_t* bits = q_idx ? reinterpret_cast<uint32_t*>(ws_at(workspace, w.bits)) : nullptr;
+    hipStream_t hs = as_stream(stream);
+    const int keep_all = thr >= 1.0f;
+
+    NABLA_LAUNCH(launch_pool(q, k, qa, ka, s.BH * s.n, (int)s.D, hs));
+    NABLA_LAUNCH(launch_logits(qa, ka, logits, s.BH, (int)s.n, (int)s.D,
+                               1.0f / sqrtf((float)s.D), hs));
+    NABLA_LAUNCH(launch_select(logits, s.BH, (int)s.n, keep_all, threshold_fixed(thr), sp, kv_count,
+                               kv_idx, dense_mask, bits, w.words_per_row, hs));
+    if (q_idx)
+        NABLA_LAUNCH(launch_transpose(bits, s.BH, (int)s.n, w.words_per_row, q_count, q_idx, hs));
+    return NABLA_OK;
+}
+
+nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t B,
+                                     int32_t H, int32_t S, int32_t D, int32_t N,
+                                     const int32_t* kv_count, const int32_t* kv_idx,
+                                     float softmax_scale, void* o, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    Shape s;
+    nabla_status_t st = check_shape(B, H, S, D, N, &s);
+    if (st != NABLA_OK) return st;
+    if (!q || !k || !v || !o || !kv_count || !kv_idx) return NABLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return NABLA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || isinf(softmax_scale)) return NABLA_ERR_INVALID_ARG;
+    const FwdWorkspace w = fwd_workspace(s);
+    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
+
+    int32_t* order = reinterpret_cast<int32_t*>(ws_at(workspace, w.order));
+    hipStream_t hs = as_stream(stream);
+    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH * s.n, (int)s.n, order, hs));
+    NABLA_LAUNCH(launch_attn_fwd(q, k, v, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx, order,
+                                 softmax_scale, o, lse, hs));
+    return NABLA_OK;
+}
+
+nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                     const void* d_o, const float* lse, int32_t B, int32_t H,
+                                     int32_t S, int32_t D, int32_t N, const int32_t* kv_count,
+                                     const int32_t* kv_idx, const int32_t* q_count,
+                                     const int32_t* q_idx, float softmax_scale, void* dq,
+                                     void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    Shape s;
+    nabla_status_t st = check_shape(B, H, S, D, N, &s);
+    if (st != NABLA_OK) return st;
+    if (!q || !k || !v || !o || !d_o || !lse || !kv_count || !kv_idx || !q_count || !q_idx ||
+        !dq || !dk || !dv)
+        return NABLA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, d_o, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return NABLA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || isinf(softmax_scale)) return NABLA_ERR_INVALID_ARG;
+    const BwdWorkspace w = bwd_workspace(s);
+    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
+
+    float* delta = reinterpret_cast<float*>(ws_at(workspace, w.delta));
+    int32_t* order_q = reinterpret_cast<int32_t*>(ws_at(workspace, w.order_q));
+    int32_t* order_kv = reinterpret_cast<int32_t*>(ws_at(workspace, w.order_kv));
+    hipStream_t hs = as_stream(stream);
+    NABLA_LAUNCH(launch_bwd_delta(o, d_o, s.BH * s.S, (int)s.D, delta, hs));
+    NABLA_LAUNCH(launch_lpt_order(q_count, s.BH * s.n, (int)s.n, order_kv, hs));
+    NABLA_LAUNCH(launch_bwd_dkdv(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, q_count, q_idx,
+                                 order_kv, softmax_scale, dk, dv, hs));
+    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH * s.n, (int)s.n, order_q, hs));
+    NABLA_LAUNCH(launch_bwd_dq(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx,
+                               order_q, softmax_scale, dq, hs));
+    return NABLA_OK;
+}
+
+}  // extern "C"

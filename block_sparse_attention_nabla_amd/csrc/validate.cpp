@@ -1,0 +1,70 @@
+// validate.cpp -- argument checks and workspace layout (no HIP dependency).
+#include "validate.h"
+
+#include <math.h>
+
+namespace nabla {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+nabla_status_t check_shape(int32_t B, int32_t H, int32_t S, int32_t D, int32_t N, Shape* out) {
+    if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || N <= 0) return NABLA_ERR_INVALID_ARG;
+    if (S % N != 0) return NABLA_ERR_INVALID_ARG;
+    if (N != 64) return NABLA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return NABLA_ERR_UNSUPPORTED;
+    const int64_t n = S / N;
+    if (n > NABLA_MAX_BLOCKS) return NABLA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    // Grid dimension limits of the kernels (one workgroup per block or row).
+    if (BH * n > (int64_t)0x7fffffff) return NABLA_ERR_UNSUPPORTED;
+    if (out) *out = Shape{B, H, S, D, N, n, BH};
+    return NABLA_OK;
+}
+
+nabla_status_t check_sta(const nabla_sta_t* sta, const Shape& s) {
+    if (!sta) return NABLA_OK;
+    if (sta->T <= 0 || sta->Hs <= 0 || sta->Ws <= 0 || sta->P <= 0) return NABLA_ERR_INVALID_ARG;
+    if ((int64_t)sta->P * sta->P != s.N) return NABLA_ERR_INVALID_ARG;
+    if (sta->Hs % sta->P || sta->Ws % sta->P) return NABLA_ERR_INVALID_ARG;
+    if ((int64_t)sta->T * sta->Hs * sta->Ws != s.S) return NABLA_ERR_INVALID_ARG;
+    if (sta->win_t < 1 || sta->win_h < sta->P || sta->win_w < sta->P) return NABLA_ERR_INVALID_ARG;
+    if (sta->win_h % sta->P || sta->win_w % sta->P) return NABLA_ERR_INVALID_ARG;
+    return NABLA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+MaskWorkspace mask_workspace(const Shape& s) {
+    MaskWorkspace w;
+    const size_t pooled = (size_t)s.BH * s.n * s.D * sizeof(float);
+    w.words_per_row = (int)((s.n + 31) / 32);
+    w.qa = 0;
+    w.ka = w.qa + align256(pooled);
+    w.logits = w.ka + align256(pooled);
+    w.bits = w.logits + align256((size_t)s.BH * s.n * s.n * sizeof(float));
+    w.total = w.bits + align256((size_t)s.BH * s.n * w.words_per_row * sizeof(uint32_t));
+    return w;
+}
+
+FwdWorkspace fwd_workspace(const Shape& s) {
+    FwdWorkspace w;
+    w.order = 0;
+    w.total = align256((size_t)s.BH * s.n * sizeof(int32_t));
+    return w;
+}
+
+BwdWorkspace bwd_workspace(const Shape& s) {
+    BwdWorkspace w;
+    w.delta = 0;
+    w.order_q = align256((size_t)s.BH * s.S * sizeof(float));
+    w.order_kv = w.order_q + align256((size_t)s.BH * s.n * sizeof(int32_t));
+    w.total = w.order_kv + align256((size_t)s.BH * s.n * sizeof(int32_t));
+    return w;
+}
+
+uint64_t threshold_fixed(float thr) {
+    const double x = (double)thr * 1099511627776.0;  // 2^40
+    return (uint64_t)floor(x);
+}
+
+}  // namespace nabla

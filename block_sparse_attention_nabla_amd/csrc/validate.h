@@ -1,0 +1,39 @@
+// validate.h -- argument checks and workspace layout of the NABLA C ABI.
+// Plain C++ with no HIP dependency: every check runs before any GPU work.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nabla.h"
+
+namespace nabla {
+
+struct Shape {
+    int64_t B, H, S, D, N, n, BH;
+};
+
+// Region offsets inside a caller-provided workspace (all 256-byte aligned).
+struct MaskWorkspace {
+    size_t qa, ka, logits, bits, total;
+    int words_per_row;
+};
+struct FwdWorkspace {
+    size_t order, total;
+};
+struct BwdWorkspace {
+    size_t delta, order_q, order_kv, total;
+};
+
+nabla_status_t check_shape(int32_t B, int32_t H, int32_t S, int32_t D, int32_t N, Shape* out);
+nabla_status_t check_sta(const nabla_sta_t* sta, const Shape& s);
+bool aligned16(const void* p);
+
+MaskWorkspace mask_workspace(const Shape& s);
+FwdWorkspace fwd_workspace(const Shape& s);
+BwdWorkspace bwd_workspace(const Shape& s);
+
+// Fixed-point threshold used by the selection kernel: floor(thr * 2^40).
+uint64_t threshold_fixed(float thr);
+
+}  // namespace nabla

@@ -1,0 +1,137 @@
+/*
+ * nabla.h -- C ABI of the MI355X (gfx950) NABLA block-sparse attention library.
+ *
+ * NABLA ("Neighborhood Adaptive Block-Level Attention", arXiv 2507.13546) makes a
+ * per-head block mask from average-pooled queries and keys (Algorithm 1,
+ * section 3.1.2), optionally ORs it with a sliding-tile (STA) mask (section
+ * 3.1.3), and runs attention only on the kept N x N blocks (eq. (4), section 2.2).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors Q, K, V, O, dO, dQ, dK, dV are device pointers to contiguous bf16
+ *    (bfloat16, 2 bytes) arrays of shape [B, H, S, D] (row-major; D fastest).
+ *    Tokens must already be in block order: block i of a head is tokens
+ *    [i*N, (i+1)*N) (the paper's token reordering, section 3.1.1, Figure 3).
+ *  - n = S / N query (and key) blocks per head. Block lists are int32:
+ *      kv_count [B, H, n]      number of kept key blocks of query block i,
+ *      kv_idx   [B, H, n, n]   entries [0, kv_count) = kept key blocks, ascending;
+ *                              later entries are unspecified (not written),
+ *      q_count  [B, H, n]      number of query blocks that keep key block j,
+ *      q_idx    [B, H, n, n]   entries [0, q_count) = those query blocks, ascending.
+ *  - Supported now: N == 64, D in {64, 128}, S % N == 0, n <= NABLA_MAX_BLOCKS.
+ *  - Ownership: the caller allocates every buffer, including the workspace
+ *    (size from nabla_workspace_size). The library never allocates, frees or
+ *    synchronises; it enqueues work on `stream` (a hipStream_t; NULL = the
+ *    default stream) and returns. It keeps no state between calls; concurrent
+ *    calls are safe when they use distinct output and workspace buffers.
+ *  - Errors: every argument is validated before anything is enqueued; a
+ *    non-OK status means nothing was launched (except NABLA_ERR_HIP, returned
+ *    when a launch itself fails). Faults inside kernels surface at the
+ *    caller's next synchronisation, as for any HIP kernel.
+ */
+#ifndef NABLA_H
+#define NABLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NABLA_MAX_BLOCKS 8192
+
+/* Symbols of this ABI are the only ones the shared library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define NABLA_API __attribute__((visibility("default")))
+#else
+#define NABLA_API
+#endif
+
+typedef enum {
+    NABLA_OK = 0,
+    NABLA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, bad threshold, bad STA geometry */
+    NABLA_ERR_UNSUPPORTED = 2, /* valid but not implemented: N != 64, D not in {64,128}, n too big */
+    NABLA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than nabla_workspace_size() */
+    NABLA_ERR_HIP = 4          /* a HIP launch or query failed */
+} nabla_status_t;
+
+/* Sliding-tile window (section 2.2, eq. (4)-(5); STA_mask(T, H, W, W_T, W_H, W_W)
+ * of section 3.1.3). The latent grid is T frames of Hs x Ws tokens, tiled by
+ * 1 x P x P tiles, so one tile is one block and N == P*P. The window is
+ * win_t frames x win_h x win_w tokens (win_h, win_w multiples of P), centred on
+ * the query tile -- (w-1)/2 tiles below, w/2 above on each axis -- and clipped
+ * at the grid edges. Requires T*Hs*Ws == S, Hs % P == 0, Ws % P == 0, windows >= 1. */
+typedef struct {
+    int32_t T, Hs, Ws, P;
+    int32_t win_t, win_h, win_w;
+} nabla_sta_t;
+
+enum { NABLA_OP_MASK = 0, NABLA_OP_FWD = 1, NABLA_OP_BWD = 2 };
+
+/* Bytes of device workspace the given operation needs (0 for invalid shapes). */
+NABLA_API size_t nabla_workspace_size(int32_t op, int32_t B, int32_t H, int32_t S, int32_t D, int32_t N);
+
+/* Human-readable name of a status code (static storage). */
+NABLA_API const char* nabla_status_string(nabla_status_t status);
+
+/*
+ * Block mask (Algorithm 1, section 3.1.2, plus the STA union of section 3.1.3).
+ * For every head and query block i:
+ *   Q_a[i] = mean of the N query rows of block i, K_a[j] likewise (steps 2-5);
+ *   p_ij   = softmax_j(Q_a[i] . K_a[j] / sqrt(D))                 (steps 6-7);
+ *   keep j iff thr >= 1 or G_ij <= thr, G_ij = sum of p_il over l with
+ *   p_il > p_ij -- the sort / cumulative-sum / ">= 1 - thr" binarisation of
+ *   steps 8-11 with ties kept together;                            then
+ *   keep j also if the STA window of i contains j (when sta != NULL).
+ * Everything after the bf16 loads is computed in fp32. Results are written as
+ * the compact lists above; q_count/q_idx (needed by the backward pass) and
+ * dense_mask (uint8 [B, H, n, n], 1 = kept) are optional (NULL = skip).
+ * thr must be finite and >= 0. Every row keeps at least its largest entry.
+ */
+NABLA_API nabla_status_t nabla_build_mask(const void* q, const void* k, int32_t B, int32_t H, int32_t S,
+                                int32_t D, int32_t N, float thr, const nabla_sta_t* sta,
+                                int32_t* kv_count, int32_t* kv_idx, int32_t* q_count,
+                                int32_t* q_idx, uint8_t* dense_mask, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse attention forward (eq. (4) with the kept-block mask): for each
+ * token s of query block i,
+ *   O_s   = sum_u softmax_u(scale * q_s . k_u) v_u over the keys u of the kept
+ *           blocks kv_idx[b, h, i, 0 .. kv_count),
+ *   LSE_s = log sum_u exp(scale * q_s . k_u)   (natural log).
+ * o: bf16 [B, H, S, D] output. lse: fp32 [B, H, S] output, may be NULL (the
+ * backward pass needs it). softmax_scale > 0, finite (the paper uses 1/sqrt(D)).
+ * Kept-block indices must lie in [0, n) and counts in [0, n]; a row with
+ * count 0 yields O = 0 and LSE = -inf. bf16 MFMA, fp32 accumulation and softmax.
+ */
+NABLA_API nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t B,
+                                     int32_t H, int32_t S, int32_t D, int32_t N,
+                                     const int32_t* kv_count, const int32_t* kv_idx,
+                                     float softmax_scale, void* o, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse attention backward: gradients of the forward with the mask held
+ * constant (the mask is a piecewise-constant function of Q and K):
+ *   P = exp(scale * Q K^T - LSE) on kept blocks, Delta_s = dO_s . O_s,
+ *   dV = P^T dO, dP = dO V^T, dS = P * (dP - Delta),
+ *   dQ = scale * dS K, dK = scale * dS^T Q.
+ * Inputs o and lse are the forward's outputs for the same q, k, v, lists and
+ * scale; d_o is the output gradient (bf16). q_count/q_idx is the transpose of
+ * kv_count/kv_idx (as produced by nabla_build_mask). dq, dk, dv: bf16 outputs.
+ * Deterministic: no atomics on the gradients.
+ */
+NABLA_API nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                     const void* d_o, const float* lse, int32_t B, int32_t H,
+                                     int32_t S, int32_t D, int32_t N, const int32_t* kv_count,
+                                     const int32_t* kv_idx, const int32_t* q_count,
+                                     const int32_t* q_idx, float softmax_scale, void* dq,
+                                     void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NABLA_H */

@@ -295,6 +295,10 @@ EXPORT void nabla_oracle_attn_bwd_dq(const float* q, const float* k, const float
 /* Gradients with respect to K and V, the mask held constant:
  *   dV_u = sum_s P_su dO_s,   dK_u = scale * sum_s dS_su q_s,
  * the sums over every token s whose query block keeps u's block.
+ * First pass: for every query row s that keeps one of the listed key blocks,
+ * its softmax statistics over all its kept keys -- maximum m_s, denominator
+ * Z_s -- and Delta_s = sum_u P_su (dO_s . v_u). Second pass: for each listed
+ * key block, P_su = exp(x_su - m_s) / Z_s and dS_su for its keys u only.
  * kv_blocks lists flattened key blocks (bh*n + j) (NULL = all); only their
  * rows of dk and dv are written. */
 EXPORT void nabla_oracle_attn_bwd_dkdv(const float* q, const float* k, const float* v,
@@ -304,49 +308,96 @@ EXPORT void nabla_oracle_attn_bwd_dkdv(const float* q, const float* k, const flo
                                        double* dv) {
     const int64_t n = S / N;
     const int64_t total = kv_blocks ? nblocks : BH * n;
+    /* query blocks whose row statistics are needed */
+    uint8_t* need = (uint8_t*)calloc((size_t)(BH * n), 1);
+    double* rm = (double*)malloc(sizeof(double) * BH * S);
+    double* rz = (double*)malloc(sizeof(double) * BH * S);
+    double* rdelta = (double*)malloc(sizeof(double) * BH * S);
+    for (int64_t t = 0; t < total; ++t) {
+        const int64_t blk = kv_blocks ? kv_blocks[t] : t;
+        const int64_t bh = blk / n, j = blk % n;
+        for (int64_t i = 0; i < n; ++i)
+            if (mask[(bh * n + i) * n + j]) need[bh * n + i] = 1;
+    }
 #pragma omp parallel
     {
         int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * S);
-        double* p = (double*)malloc(sizeof(double) * S);
-        double* dp = (double*)malloc(sizeof(double) * S);
-#pragma omp for schedule(dynamic, 1)
-        for (int64_t t = 0; t < total; ++t) {
-            const int64_t blk = kv_blocks ? kv_blocks[t] : t;
-            const int64_t bh = blk / n, j = blk % n;
-            const float* kbh = k + bh * S * D;
-            const float* vbh = v + bh * S * D;
+        double* x = (double*)malloc(sizeof(double) * S);
+#pragma omp for collapse(2) schedule(dynamic, 4)
+        for (int64_t qb = 0; qb < BH * n; ++qb) {
             for (int64_t r = 0; r < N; ++r) {
-                double* dku = dk + (bh * S + j * N + r) * D;
-                double* dvu = dv + (bh * S + j * N + r) * D;
-                for (int64_t d = 0; d < D; ++d) dku[d] = dvu[d] = 0.0;
+                if (!need[qb]) continue;
+                const int64_t bh = qb / n, i = qb % n;
+                const int64_t nk = kept_keys(mask + qb * n, n, N, keys);
+                const int64_t s = i * N + r;
+                const float* qs = q + (bh * S + s) * D;
+                const float* dos = dout + (bh * S + s) * D;
+                double m = -INFINITY;
+                for (int64_t c = 0; c < nk; ++c) {
+                    const float* ku = k + (bh * S + keys[c]) * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += (double)qs[d] * (double)ku[d];
+                    x[c] = scale * dot;
+                    if (x[c] > m) m = x[c];
+                }
+                double z = 0.0;
+                for (int64_t c = 0; c < nk; ++c) {
+                    x[c] = exp(x[c] - m);
+                    z += x[c];
+                }
+                double dl = 0.0;
+                for (int64_t c = 0; c < nk; ++c) {
+                    const float* vu = v + (bh * S + keys[c]) * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += (double)dos[d] * (double)vu[d];
+                    dl += (x[c] / z) * dot;
+                }
+                rm[bh * S + s] = m;
+                rz[bh * S + s] = z;
+                rdelta[bh * S + s] = dl;
             }
-            for (int64_t i = 0; i < n; ++i) {
-                const uint8_t* mrow = mask + (bh * n + i) * n;
-                if (!mrow[j]) continue;
-                const int64_t nk = kept_keys(mrow, n, N, keys);
-                int64_t first = 0;  /* position of block j's first key in the kept list */
-                while (keys[first] != j * N) ++first;
-                for (int64_t rq = 0; rq < N; ++rq) {
-                    const int64_t s = i * N + rq;
-                    const float* qs = q + (bh * S + s) * D;
-                    const float* dos = dout + (bh * S + s) * D;
-                    double delta;
-                    row_probs(qs, dos, kbh, vbh, keys, nk, D, scale, p, dp, &delta);
-                    for (int64_t r = 0; r < N; ++r) {
-                        const int64_t c = first + r;
-                        const double ds = p[c] * (dp[c] - delta);
-                        double* dku = dk + (bh * S + j * N + r) * D;
-                        double* dvu = dv + (bh * S + j * N + r) * D;
-                        for (int64_t d = 0; d < D; ++d) {
-                            dvu[d] += p[c] * (double)dos[d];
-                            dku[d] += scale * ds * (double)qs[d];
-                        }
+        }
+        free(keys);
+        free(x);
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < total; ++t) {
+        const int64_t blk = kv_blocks ? kv_blocks[t] : t;
+        const int64_t bh = blk / n, j = blk % n;
+        for (int64_t r = 0; r < N; ++r) {
+            double* dku = dk + (bh * S + j * N + r) * D;
+            double* dvu = dv + (bh * S + j * N + r) * D;
+            for (int64_t d = 0; d < D; ++d) dku[d] = dvu[d] = 0.0;
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            if (!mask[(bh * n + i) * n + j]) continue;
+            for (int64_t rq = 0; rq < N; ++rq) {
+                const int64_t s = i * N + rq;
+                const float* qs = q + (bh * S + s) * D;
+                const float* dos = dout + (bh * S + s) * D;
+                for (int64_t r = 0; r < N; ++r) {
+                    const int64_t u = j * N + r;
+                    const float* ku = k + (bh * S + u) * D;
+                    const float* vu = v + (bh * S + u) * D;
+                    double xs = 0.0, dp = 0.0;
+                    for (int64_t d = 0; d < D; ++d) {
+                        xs += (double)qs[d] * (double)ku[d];
+                        dp += (double)dos[d] * (double)vu[d];
+                    }
+                    const double p = exp(scale * xs - rm[bh * S + s]) / rz[bh * S + s];
+                    const double ds = p * (dp - rdelta[bh * S + s]);
+                    double* dku = dk + (bh * S + u) * D;
+                    double* dvu = dv + (bh * S + u) * D;
+                    for (int64_t d = 0; d < D; ++d) {
+                        dvu[d] += p * (double)dos[d];
+                        dku[d] += scale * ds * (double)qs[d];
                     }
                 }
             }
         }
-        free(keys);
-        free(p);
-        free(dp);
     }
+    free(need);
+    free(rm);
+    free(rz);
+    free(rdelta);
 }

@@ -1,0 +1,146 @@
+"""The C ABI without a GPU: the library loads, exports exactly what include/nabla.h
+declares, sizes workspaces, and rejects bad arguments with status codes before
+any GPU work is enqueued (only validation paths are exercised here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_nabla_amd as nb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nabla.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nb.LIB_PATH):
+        pytest.fail("libnabla.so is not built (run python -m block_sparse_attention_nabla_amd.build)")
+    return nb.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"NABLA_API\s+[\w\s\*]+?\b(nabla_\w+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    declared = _declared_functions()
+    assert declared == sorted(nb.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", nb.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T " in ln and "nabla" in ln})
+    assert exported == declared
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    assert nb.nabla_status_string(0) == "NABLA_OK"
+    assert nb.nabla_status_string(3) == "NABLA_ERR_WORKSPACE"
+    assert nb.nabla_status_string(99) == "NABLA_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(lib):
+    B, H, S, D = 1, 2, 1024, 64
+    n = S // 64
+    mask = nb.nabla_workspace_size(nb.NABLA_OP_MASK, B, H, S, D)
+    assert mask >= 2 * B * H * n * D * 4 + B * H * n * n * 4
+    assert nb.nabla_workspace_size(nb.NABLA_OP_FWD, B, H, S, D) >= B * H * n * 4
+    assert nb.nabla_workspace_size(nb.NABLA_OP_BWD, B, H, S, D) >= B * H * S * 4 + 2 * B * H * n * 4
+    assert nb.nabla_workspace_size(nb.NABLA_OP_MASK, B, H, 1000, D) == 0  # S % N != 0
+    assert nb.nabla_workspace_size(nb.NABLA_OP_MASK, B, H, S, 96) == 0    # unsupported D
+    assert nb.nabla_workspace_size(7, B, H, S, D) == 0
+
+
+# Fake, 256-aligned, never-dereferenced device addresses: every call below
+# fails validation before anything touches them.
+P = ctypes.c_void_p(0x7F0000000000)
+P2 = ctypes.c_void_p(0x7F0000100000)
+BIG = 1 << 40
+
+
+def _mask(lib, B=1, H=2, S=1024, D=64, N=64, thr=0.5, sta=None, q=P, k=P, cnt=P, idx=P,
+          qc=None, qi=None, ws=P2, wsb=BIG):
+    return lib.nabla_build_mask(q, k, B, H, S, D, N, thr, sta, cnt, idx, qc, qi, None, ws, wsb, None)
+
+
+def test_build_mask_validation(lib):
+    assert _mask(lib, S=1000) == INVALID
+    assert _mask(lib, B=0) == INVALID
+    assert _mask(lib, N=32, S=1024) == UNSUPPORTED
+    assert _mask(lib, D=96) == UNSUPPORTED
+    assert _mask(lib, S=64 * (8192 + 1)) == UNSUPPORTED
+    assert _mask(lib, thr=float("nan")) == INVALID
+    assert _mask(lib, thr=-0.01) == INVALID
+    assert _mask(lib, thr=float("inf")) == INVALID
+    assert _mask(lib, q=None) == INVALID
+    assert _mask(lib, idx=None) == INVALID
+    assert _mask(lib, q=ctypes.c_void_p(0x7F0000000008)) == INVALID  # not 16-byte aligned
+    assert _mask(lib, qc=P, qi=None) == INVALID
+    assert _mask(lib, ws=None) == WORKSPACE
+    assert _mask(lib, wsb=16) == WORKSPACE
+
+
+def test_build_mask_sta_validation(lib):
+    good = dict(T=4, Hs=16, Ws=16, P=8, win_t=3, win_h=8, win_w=8)
+
+    def sta(**over):
+        d = dict(good, **over)
+        return ctypes.pointer(nb.StaWindow(*(d[f] for f in ("T", "Hs", "Ws", "P", "win_t", "win_h", "win_w"))))
+
+    # S = 4*16*16 = 1024 matches; every bad field is rejected.
+    assert _mask(lib, sta=sta(T=5)) == INVALID         # T*Hs*Ws != S
+    assert _mask(lib, sta=sta(P=4)) == INVALID         # P*P != N
+    assert _mask(lib, sta=sta(win_h=12)) == INVALID    # not a multiple of P
+    assert _mask(lib, sta=sta(win_t=0)) == INVALID
+    assert _mask(lib, sta=sta(win_w=0)) == INVALID
+    assert _mask(lib, sta=sta(Hs=12, Ws=16 * 16 // 12)) == INVALID
+
+
+def test_fwd_validation(lib):
+    f = lib.nabla_sparse_attn_fwd
+
+    def call(S=1024, D=64, scale=0.125, v=P, o=P, ws=P2, wsb=BIG):
+        return f(P, P, v, 1, 2, S, D, 64, P, P, scale, o, None, ws, wsb, None)
+
+    assert call(S=1000) == INVALID
+    assert call(D=256) == UNSUPPORTED
+    assert call(scale=0.0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(v=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=4) == WORKSPACE
+
+
+def test_bwd_validation(lib):
+    f = lib.nabla_sparse_attn_bwd
+
+    def call(S=1024, lse=P, qc=P, scale=0.125, ws=P2, wsb=BIG):
+        return f(P, P, P, P, P, lse, 1, 2, S, 64, 64, P, P, qc, P, scale, P, P, P, ws, wsb, None)
+
+    assert call(S=1000) == INVALID
+    assert call(lse=None) == INVALID
+    assert call(qc=None) == INVALID
+    assert call(scale=-1.0) == INVALID
+    assert call(wsb=8) == WORKSPACE
+
+
+def test_binding_requires_the_library(tmp_path):
+    # The binding never falls back to anything else: a missing library raises.
+    import importlib
+    mod = importlib.import_module("block_sparse_attention_nabla_amd")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.load_library(str(tmp_path / "nope.so"))
+    finally:
+        mod._lib = saved

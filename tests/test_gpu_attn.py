@@ -1,0 +1,213 @@
+"""GPU parity of block-sparse attention (forward and backward) against the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (GRAD_MAX_ABS, GRAD_REL_L2, LSE_MAX_ABS, O_MAX_ABS, O_MEAN_ABS, attn_errors,
+                    grad_errors, lists_to_mask)
+
+pytestmark = pytest.mark.gpu
+
+
+def _nb():
+    import block_sparse_attention_nabla_amd as nb
+    nb.load_library()
+    return nb
+
+
+def _lists_from_mask(mask: np.ndarray, B, H):
+    lists = oracle.mask_to_lists(mask)
+    n = mask.shape[-1]
+    out = {}
+    for key in ("kv_count", "q_count"):
+        out[key] = torch.from_numpy(lists[key].reshape(B, H, n)).cuda()
+    for key in ("kv_idx", "q_idx"):
+        out[key] = torch.from_numpy(lists[key].reshape(B, H, n, n)).cuda()
+    return out
+
+
+def _rand(B, H, S, D, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return [(torch.randn((B, H, S, D), generator=g) * scale).bfloat16() for _ in range(4)]
+
+
+def _random_mask(BH, n, seed, p):
+    rng = np.random.default_rng(seed)
+    m = (rng.random((BH, n, n)) < p).astype(np.uint8)
+    m[:, np.arange(n), rng.integers(0, n, n)] = 1  # every row keeps something
+    return m
+
+
+def _fwd_check(q, k, v, lists, mask, scale=None, tag=""):
+    nb = _nb()
+    B, H, S, D = q.shape
+    print(f"[fwd] {tag} shape={tuple(q.shape)} kept={int(mask.sum())}", flush=True)
+    o, lse = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"],
+                                      softmax_scale=scale)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.attn_fwd(q.float(), k.float(), v.float(), mask, 64, scale=scale)
+    e = attn_errors(o.float().cpu().numpy().reshape(B * H, S, D), ro)
+    dl = np.abs(lse.cpu().numpy().reshape(B * H, S) - rlse)
+    print(f"[fwd] {tag} {e} lse_max_abs={dl.max():.2e}", flush=True)
+    assert e["max_abs"] <= O_MAX_ABS and e["mean_abs"] <= O_MEAN_ABS, e
+    assert dl.max() <= LSE_MAX_ABS
+    return o, lse
+
+
+@pytest.mark.parametrize("thr", [0.2, 0.5, 0.9, 1.0])
+def test_fwd_tiny_with_gpu_mask(thr):
+    nb = _nb()
+    w = synth.get_workload("tiny")
+    x = synth.make_inputs(w)
+    q, k, v = (x[key].bfloat16() for key in ("q", "k", "v"))
+    lists = nb.nabla_build_mask(q.cuda(), k.cuda(), thr, transpose=True)
+    torch.cuda.synchronize()
+    mask = lists_to_mask(lists["kv_count"].cpu().numpy(), lists["kv_idx"].cpu().numpy())
+    _fwd_check(q, k, v, lists, mask, tag=f"tiny thr={thr}")
+
+
+@pytest.mark.parametrize("name", ["dit_small", "dit_small_sta"])
+def test_fwd_dit_small_with_gpu_mask(name):
+    nb = _nb()
+    w = synth.get_workload(name)
+    x = synth.make_inputs(w)
+    thr = w.thresholds()[0]
+    lists = nb.nabla_build_mask(x["q"].cuda(), x["k"].cuda(), thr, w.sta_struct())
+    torch.cuda.synchronize()
+    mask = lists_to_mask(lists["kv_count"].cpu().numpy(), lists["kv_idx"].cpu().numpy())
+    _fwd_check(x["q"], x["k"], x["v"], lists, mask, tag=name)
+
+
+@pytest.mark.parametrize("B,H,n,D,p", [(1, 2, 9, 64, 0.4), (2, 1, 33, 128, 0.3), (1, 1, 1, 128, 1.0),
+                                       (1, 3, 70, 64, 0.15)])
+def test_fwd_random_masks(B, H, n, D, p):
+    q, k, v, _ = _rand(B, H, 64 * n, D, seed=n + D, scale=1.5)
+    mask = _random_mask(B * H, n, n, p)
+    _fwd_check(q, k, v, _lists_from_mask(mask, B, H), mask, tag="random")
+
+
+def test_fwd_keep_all_equals_dense_and_custom_scale():
+    q, k, v, _ = _rand(1, 2, 64 * 12, 128, seed=11, scale=2.0)
+    mask = np.ones((2, 12, 12), dtype=np.uint8)
+    _fwd_check(q, k, v, _lists_from_mask(mask, 1, 2), mask, scale=0.05, tag="dense scale=0.05")
+
+
+def test_fwd_empty_rows_give_zero_and_minus_inf():
+    nb = _nb()
+    q, k, v, _ = _rand(1, 1, 64 * 4, 64, seed=12)
+    mask = np.eye(4, dtype=np.uint8)[None]
+    lists = _lists_from_mask(mask, 1, 1)
+    lists["kv_count"][0, 0, 2] = 0
+    o, lse = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"])
+    torch.cuda.synchronize()
+    assert torch.all(o[0, 0, 128:192] == 0)
+    assert torch.all(torch.isneginf(lse[0, 0, 128:192]))
+    mask[0, 2, 2] = 0
+    ro, _ = oracle.attn_fwd(q.float(), k.float(), v.float(), np.maximum(mask, np.eye(4, dtype=np.uint8)), 64)
+    e = attn_errors(o.float().cpu().numpy()[0, 0, :128], ro[0, :128])
+    assert e["max_abs"] <= O_MAX_ABS
+
+
+def test_fwd_values_in_dropped_blocks_are_never_read():
+    nb = _nb()
+    q, k, v, _ = _rand(1, 1, 64 * 6, 128, seed=13)
+    mask = np.zeros((1, 6, 6), dtype=np.uint8)
+    mask[0, :, 1] = 1
+    mask[0, :, 4] = 1
+    lists = _lists_from_mask(mask, 1, 1)
+    o1, _ = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"])
+    v2 = v.clone()
+    v2[:, :, 128:256] = float("nan")
+    o2, _ = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v2.cuda(), lists["kv_count"], lists["kv_idx"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_fwd_is_deterministic():
+    nb = _nb()
+    q, k, v, _ = _rand(1, 4, 64 * 40, 128, seed=14)
+    mask = _random_mask(4, 40, 15, 0.3)
+    lists = _lists_from_mask(mask, 1, 4)
+    a = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"])
+    b = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ backward
+def _bwd_check(q, k, v, do, lists, mask, tag="", q_blocks=None, kv_blocks=None):
+    nb = _nb()
+    B, H, S, D = q.shape
+    print(f"[bwd] {tag} shape={tuple(q.shape)} kept={int(mask.sum())}", flush=True)
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = nb.nabla_sparse_attn_fwd(qg, kg, vg, lists["kv_count"], lists["kv_idx"])
+    dq, dk, dv = nb.nabla_sparse_attn_bwd(qg, kg, vg, o, dog, lse, lists["kv_count"], lists["kv_idx"],
+                                          lists["q_count"], lists["q_idx"])
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.attn_bwd(q.float(), k.float(), v.float(), do.float(), mask, 64,
+                                    q_blocks=q_blocks, kv_blocks=kv_blocks)
+    res = {}
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        gg = g.float().cpu().numpy().reshape(B * H, S, D)
+        sel = ~np.isnan(r[..., 0])
+        res[name] = grad_errors(gg[sel], r[sel])
+    print(f"[bwd] {tag} {res}", flush=True)
+    for name, e in res.items():
+        assert e["rel_l2"] <= GRAD_REL_L2 and e["max_abs"] <= GRAD_MAX_ABS, (name, e)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("thr", [0.5, 1.0])
+def test_bwd_tiny_with_gpu_mask(thr):
+    nb = _nb()
+    w = synth.get_workload("tiny")
+    x = synth.make_inputs(w)
+    q, k, v = (x[key].bfloat16() for key in ("q", "k", "v"))
+    do = synth.make_dout(w).bfloat16()
+    lists = nb.nabla_build_mask(q.cuda(), k.cuda(), thr, transpose=True)
+    torch.cuda.synchronize()
+    mask = lists_to_mask(lists["kv_count"].cpu().numpy(), lists["kv_idx"].cpu().numpy())
+    _bwd_check(q, k, v, do, lists, mask, tag=f"tiny thr={thr}")
+
+
+@pytest.mark.parametrize("B,H,n,D,p", [(1, 2, 9, 64, 0.4), (2, 1, 21, 128, 0.3), (1, 1, 1, 64, 1.0)])
+def test_bwd_random_masks(B, H, n, D, p):
+    q, k, v, do = _rand(B, H, 64 * n, D, seed=100 + n + D)
+    mask = _random_mask(B * H, n, 200 + n, p)
+    _bwd_check(q, k, v, do, _lists_from_mask(mask, B, H), mask, tag="random")
+
+
+def test_bwd_dit_small_sampled():
+    # Full dit_small shape with the GPU mask; oracle gradients on sampled blocks.
+    nb = _nb()
+    w = synth.get_workload("dit_small")
+    x = synth.make_inputs(w)
+    do = synth.make_dout(w)
+    lists = nb.nabla_build_mask(x["q"].cuda(), x["k"].cuda(), w.thresholds()[0], transpose=True)
+    torch.cuda.synchronize()
+    mask = lists_to_mask(lists["kv_count"].cpu().numpy(), lists["kv_idx"].cpu().numpy())
+    rng = np.random.default_rng(0)
+    blocks = sorted(rng.choice(w.B * w.H * w.n, 24, replace=False).tolist())
+    _bwd_check(x["q"], x["k"], x["v"], do, lists, mask, tag="dit_small", q_blocks=blocks,
+               kv_blocks=blocks)
+
+
+def test_bwd_is_deterministic():
+    nb = _nb()
+    q, k, v, do = _rand(1, 2, 64 * 30, 128, seed=300)
+    mask = _random_mask(2, 30, 301, 0.3)
+    lists = _lists_from_mask(mask, 1, 2)
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = nb.nabla_sparse_attn_fwd(qg, kg, vg, lists["kv_count"], lists["kv_idx"])
+    a = nb.nabla_sparse_attn_bwd(qg, kg, vg, o, dog, lse, lists["kv_count"], lists["kv_idx"],
+                                 lists["q_count"], lists["q_idx"])
+    b = nb.nabla_sparse_attn_bwd(qg, kg, vg, o, dog, lse, lists["kv_count"], lists["kv_idx"],
+                                 lists["q_count"], lists["q_idx"])
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -1,0 +1,162 @@
+"""GPU parity of the mask stage: nabla_build_mask against the CPU oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import compare_masks, lists_to_mask
+
+pytestmark = pytest.mark.gpu
+
+
+def _nb():
+    import block_sparse_attention_nabla_amd as nb
+    nb.load_library()
+    return nb
+
+
+def _run(q_bf16, k_bf16, thr, sta=None):
+    """GPU mask (dense + lists + transpose) and the oracle on the same bf16 values."""
+    nb = _nb()
+    print(f"[mask] shape={tuple(q_bf16.shape)} thr={thr} sta={sta}", flush=True)
+    qg, kg = q_bf16.cuda(), k_bf16.cuda()
+    out = nb.nabla_build_mask(qg, kg, thr, sta, transpose=True, dense=True)
+    torch.cuda.synchronize()
+    gpu = {key: val.cpu().numpy() for key, val in out.items()}
+    orc = oracle.build_mask(q_bf16.float(), k_bf16.float(), 64, thr, sta=sta)
+    return gpu, orc
+
+
+def _check_lists(gpu):
+    B, H, n = gpu["kv_count"].shape
+    dense = gpu["dense_mask"].reshape(B * H, n, n)
+    m = lists_to_mask(gpu["kv_count"], gpu["kv_idx"])
+    np.testing.assert_array_equal(m, dense)  # lists are exactly the dense mask, ascending
+    mt = lists_to_mask(gpu["q_count"], gpu["q_idx"])
+    np.testing.assert_array_equal(mt, np.swapaxes(dense, 1, 2))  # exact transpose
+    assert (gpu["kv_count"] >= 1).all(), "every row keeps its largest entry"
+    return dense
+
+
+def _assert_parity(gpu, orc, thr, sta_map=None):
+    dense = _check_lists(gpu)
+    res = compare_masks(dense, orc, thr, sta_map)
+    print(f"[mask] {res}", flush=True)
+    assert res["unexplained"] == 0, res
+    return res
+
+
+@pytest.mark.parametrize("thr", [0.2, 0.5, 0.9, 1.0])
+def test_mask_tiny_threshold_sweep(thr):
+    w = synth.get_workload("tiny")
+    x = synth.make_inputs(w)
+    gpu, orc = _run(x["q"].bfloat16(), x["k"].bfloat16(), thr)
+    _assert_parity(gpu, orc, thr)
+    if thr >= 1.0:
+        assert gpu["dense_mask"].all()
+
+
+@pytest.mark.parametrize("name", ["dit_small", "dit_small_std3"])
+def test_mask_dit_small(name):
+    w = synth.get_workload(name)
+    x = synth.make_inputs(w)
+    thr = w.thresholds()[0]
+    gpu, orc = _run(x["q"], x["k"], thr)
+    res = _assert_parity(gpu, orc, thr)
+    sparsity = 1.0 - res["kept_gpu"] / res["blocks"]
+    assert abs(sparsity - 0.80) < 0.01
+
+
+def test_mask_with_sta_union():
+    w = synth.get_workload("dit_small_sta")
+    x = synth.make_inputs(w)
+    thr = w.thresholds()[0]
+    sta = w.sta_struct()
+    gpu, orc = _run(x["q"], x["k"], thr, sta)
+    sta_map = oracle.sta_mask(**{k: sta[k] for k in ("T", "Hs", "Ws", "P", "win_t", "win_h", "win_w")})
+    _assert_parity(gpu, orc, thr, sta_map)
+    dense = gpu["dense_mask"].reshape(-1, w.n, w.n).astype(bool)
+    assert np.all(dense[:, sta_map.astype(bool)])  # the union contains the STA window
+    counts = gpu["kv_count"].reshape(-1)
+    assert counts.min() >= 24 and counts.max() <= w.n
+
+
+def _random_inputs(B, H, S, D, seed, scale=1.0, smooth=True):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, H, S, D), generator=g) * scale
+    k = torch.randn((B, H, S, D), generator=g) * scale
+    if smooth:  # correlate the tokens of each block a little
+        base = torch.randn((B, H, S // 64, 1, D), generator=g) * scale
+        q = (q.reshape(B, H, S // 64, 64, D) + base).reshape(B, H, S, D)
+        k = (k.reshape(B, H, S // 64, 64, D) + base).reshape(B, H, S, D)
+    return q.bfloat16(), k.bfloat16()
+
+
+@pytest.mark.parametrize("B,H,n,D", [(2, 3, 37, 64), (1, 2, 300, 128), (1, 1, 1, 128), (1, 1, 2, 64),
+                                     (1, 2, 257, 128)])
+def test_mask_ragged_shapes(B, H, n, D):
+    # n not a multiple of 32 / 64 / 256 exercises every tail of the kernels.
+    q, k = _random_inputs(B, H, 64 * n, D, seed=n * 7 + D)
+    for thr in (0.3, 0.75):
+        gpu, orc = _run(q, k, thr)
+        _assert_parity(gpu, orc, thr)
+
+
+def test_mask_threshold_zero_keeps_row_maximum_only():
+    q, k = _random_inputs(1, 2, 64 * 40, 128, seed=3)
+    gpu, orc = _run(q, k, 0.0)
+    _assert_parity(gpu, orc, 0.0)
+    # Without exact ties the argmax is the only block with G = 0.
+    assert (gpu["kv_count"] == 1).all()
+    am = orc["a"].argmax(-1)
+    np.testing.assert_array_equal(gpu["kv_idx"].reshape(2, 40, 40)[:, :, 0], am)
+
+
+def test_mask_keep_all_above_one():
+    q, k = _random_inputs(1, 2, 64 * 20, 64, seed=4)
+    for thr in (1.0, 3.5):
+        gpu, _ = _run(q, k, thr)
+        assert gpu["dense_mask"].all()
+        assert (gpu["kv_count"] == 20).all()
+
+
+def test_mask_exact_ties_are_kept_together():
+    # Identical key blocks give exactly tied reduced probabilities: the tie group
+    # is kept or dropped as a whole on both sides.
+    B, H, n, D = 1, 1, 16, 64
+    q, k = _random_inputs(B, H, 64 * n, D, seed=5)
+    k = k.reshape(B, H, n, 64, D)
+    k[:, :, 8:] = k[:, :, :8].clone()
+    k = k.reshape(B, H, 64 * n, D).contiguous()
+    for thr in (0.2, 0.5, 0.8):
+        gpu, orc = _run(q, k, thr)
+        res = _assert_parity(gpu, orc, thr)
+        dense = gpu["dense_mask"].reshape(n, n)
+        np.testing.assert_array_equal(dense[:, :8], dense[:, 8:])
+
+
+def test_mask_is_deterministic():
+    nb = _nb()
+    q, k = _random_inputs(1, 4, 64 * 150, 128, seed=6)
+    qg, kg = q.cuda(), k.cuda()
+    a = nb.nabla_build_mask(qg, kg, 0.6, transpose=True, dense=True)
+    b = nb.nabla_build_mask(qg, kg, 0.6, transpose=True, dense=True)
+    torch.cuda.synchronize()
+    for key in ("kv_count", "dense_mask", "q_count"):
+        assert torch.equal(a[key], b[key])
+
+
+def test_mask_row_constant_key_shift_invariance():
+    # K + c for one vector c shifts each reduced-logit row by a constant: the
+    # GPU mask must not change beyond the parity band.
+    q, k = _random_inputs(1, 2, 64 * 48, 64, seed=7)
+    c = torch.randn((1, 1, 1, 64), generator=torch.Generator().manual_seed(8)).bfloat16()
+    k2 = (k.float() + c.float()).bfloat16()
+    g1, orc1 = _run(q, k, 0.5)
+    g2, orc2 = _run(q, k2, 0.5)
+    r1 = compare_masks(g2["dense_mask"].reshape(orc1["mask"].shape), orc2, 0.5)
+    assert r1["unexplained"] == 0, r1

@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libnabla.so")
 
 NABLA_OK = 0
 NABLA_OP_MASK, NABLA_OP_FWD, NABLA_OP_BWD = 0, 1, 2
+NABLA_DTYPE_BF16, NABLA_DTYPE_FP32 = 0, 1
 BLOCK_N = 64
 
 EXPORTED_SYMBOLS = (
@@ -73,9 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.c_size_t, _vp]
     lib.nabla_sparse_attn_fwd.restype = ctypes.c_int
     lib.nabla_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
-                                          ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                          ctypes.c_float, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp]
     lib.nabla_sparse_attn_bwd.restype = ctypes.c_int
-    lib.nabla_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+    lib.nabla_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                           _vp, ctypes.c_size_t, _vp]
     _lib = lib
@@ -164,9 +165,12 @@ def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           kv_count: torch.Tensor, kv_idx: torch.Tensor,
                           softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
                           o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          want_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                          want_lse: bool = True, out_dtype: torch.dtype = torch.bfloat16,
+                          workspace: Optional[torch.Tensor] = None,
                           stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Block-sparse attention forward (eq. (4) on the kept blocks). Returns (O bf16, LSE fp32)."""
+    """Block-sparse attention forward (eq. (4) on the kept blocks).
+
+    Returns (O, LSE fp32); O is bf16 or fp32 (``out_dtype``)."""
     _check_qkv("q", q)
     B, H, S, D = q.shape
     _check_qkv("k", k, q.shape)
@@ -179,14 +183,19 @@ def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if not (kv_count.is_contiguous() and kv_idx.is_contiguous()):
         raise ValueError("kv_count / kv_idx must be contiguous")
     scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if o.dtype != out_dtype or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor of q's shape and out_dtype")
+    o_dtype = NABLA_DTYPE_FP32 if out_dtype == torch.float32 else NABLA_DTYPE_BF16
     if want_lse and lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     ws, size = _workspace(NABLA_OP_FWD, B, H, S, D, N, q.device, workspace)
     st = load_library().nabla_sparse_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), B, H, S, D, N, _ptr(kv_count), _ptr(kv_idx), scale, _ptr(o),
-        _ptr(lse) if want_lse else None, _ptr(ws), ws.numel(), _stream(q, stream))
+        o_dtype, _ptr(lse) if want_lse else None, _ptr(ws), ws.numel(), _stream(q, stream))
     if st != NABLA_OK:
         raise NablaError(st, "nabla_sparse_attn_fwd")
     return o, (lse if want_lse else None)
@@ -196,11 +205,17 @@ def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx
                           softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
                           dq=None, dk=None, dv=None, workspace=None,
                           stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Block-sparse attention backward with the mask held constant. Returns (dQ, dK, dV) bf16."""
+    """Block-sparse attention backward with the mask held constant. Returns (dQ, dK, dV) bf16.
+
+    ``o`` is the forward output, bf16 or fp32."""
     _check_qkv("q", q)
     B, H, S, D = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+    for name, t in (("k", k), ("v", v), ("d_o", d_o)):
         _check_qkv(name, t, q.shape)
+    if o.dtype not in (torch.bfloat16, torch.float32) or tuple(o.shape) != tuple(q.shape) \
+            or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous bf16 or fp32 CUDA tensor of q's shape")
+    o_dtype = NABLA_DTYPE_FP32 if o.dtype == torch.float32 else NABLA_DTYPE_BF16
     n = S // N
     for name, t, shp in (("kv_count", kv_count, (B, H, n)), ("kv_idx", kv_idx, (B, H, n, n)),
                          ("q_count", q_count, (B, H, n)), ("q_idx", q_idx, (B, H, n, n))):
@@ -214,7 +229,7 @@ def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx
     dv = torch.empty_like(q) if dv is None else dv
     ws, size = _workspace(NABLA_OP_BWD, B, H, S, D, N, q.device, workspace)
     st = load_library().nabla_sparse_attn_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), B, H, S, D, N, _ptr(kv_count),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), o_dtype, _ptr(d_o), _ptr(lse), B, H, S, D, N, _ptr(kv_count),
         _ptr(kv_idx), _ptr(q_count), _ptr(q_idx), scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
         ws.numel(), _stream(q, stream))
     if st != NABLA_OK:

@@ -102,10 +102,11 @@ __device__ __forceinline__ void store_t_acc(uint16_t* row_ptr, const f32x16_t* a
 }
 
 // ---------------------------------------------------------------------------
-// Delta_s = dO_s . O_s (fp32). D/8 lanes per row, one 16-byte chunk each.
+// Delta_s = dO_s . O_s (fp32). D/8 lanes per row, 8 elements each; O is bf16
+// or fp32 (an fp32 forward output keeps Delta free of O's bf16 rounding).
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ o,
+template <int D, bool O_FP32>
+__global__ __launch_bounds__(256) void delta_kernel(const void* __restrict__ o,
                                                     const uint16_t* __restrict__ d_o, int64_t rows,
                                                     float* __restrict__ delta) {
     constexpr int LPR = D / 8;  // lanes per row
@@ -114,13 +115,28 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
     const int part = (int)(gid % LPR);
     float s = 0.f;
     if (row < rows) {
-        const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + part * 8);
+        float ov[8];
+        if constexpr (O_FP32) {
+            const float* op = static_cast<const float*>(o) + row * D + part * 8;
+            const float4 a0 = *reinterpret_cast<const float4*>(op);
+            const float4 a1 = *reinterpret_cast<const float4*>(op + 4);
+            ov[0] = a0.x; ov[1] = a0.y; ov[2] = a0.z; ov[3] = a0.w;
+            ov[4] = a1.x; ov[5] = a1.y; ov[6] = a1.z; ov[7] = a1.w;
+        } else {
+            const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(o) + row * D + part * 8);
+            const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ov[2 * e] = bf16_bits_to_f32(wa[e] & 0xffffu);
+                ov[2 * e + 1] = bf16_bits_to_f32(wa[e] >> 16);
+            }
+        }
         const uint4 b = *reinterpret_cast<const uint4*>(d_o + row * D + part * 8);
-        const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+        const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            s += bf16_bits_to_f32(wa[e] & 0xffffu) * bf16_bits_to_f32(wb[e] & 0xffffu);
-            s += bf16_bits_to_f32(wa[e] >> 16) * bf16_bits_to_f32(wb[e] >> 16);
+            s += ov[2 * e] * bf16_bits_to_f32(wb[e] & 0xffffu);
+            s += ov[2 * e + 1] * bf16_bits_to_f32(wb[e] >> 16);
         }
     }
 #pragma unroll
@@ -299,14 +315,18 @@ __global__ __launch_bounds__(128) void dq_kernel(
     store_t_acc<DT>(dq + head + (int64_t)qrow * D, dQt, scale, h);
 }
 
-hipError_t launch_bwd_delta(const void* o, const void* d_o, int64_t rows, int D, float* delta,
-                            hipStream_t stream) {
+hipError_t launch_bwd_delta(const void* o, bool o_fp32, const void* d_o, int64_t rows, int D,
+                            float* delta, hipStream_t stream) {
     const int64_t threads = rows * (D / 8);
     const unsigned grid = (unsigned)((threads + 255) / 256);
-    if (D == 128)
-        delta_kernel<128><<<grid, 256, 0, stream>>>((const uint16_t*)o, (const uint16_t*)d_o, rows, delta);
-    else
-        delta_kernel<64><<<grid, 256, 0, stream>>>((const uint16_t*)o, (const uint16_t*)d_o, rows, delta);
+    const uint16_t* dop = (const uint16_t*)d_o;
+    if (D == 128) {
+        if (o_fp32) delta_kernel<128, true><<<grid, 256, 0, stream>>>(o, dop, rows, delta);
+        else delta_kernel<128, false><<<grid, 256, 0, stream>>>(o, dop, rows, delta);
+    } else {
+        if (o_fp32) delta_kernel<64, true><<<grid, 256, 0, stream>>>(o, dop, rows, delta);
+        else delta_kernel<64, false><<<grid, 256, 0, stream>>>(o, dop, rows, delta);
+    }
     return hipGetLastError();
 }
 

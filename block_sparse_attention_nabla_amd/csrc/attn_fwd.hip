@@ -69,7 +69,7 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int S, int n, const int32_t* __restrict__ kv_count,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ order, float scale_log2,
-    uint16_t* __restrict__ o, float* __restrict__ lse) {
+    void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
     constexpr int KST = FwdTile<D>::KST, VST = FwdTile<D>::VST;
     constexpr int KK = D / 16;  // MFMA k-steps over the head dimension
     constexpr int DT = D / 32;  // 32-row d tiles of O^T
@@ -97,7 +97,9 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
     f32x16_t oacc[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[t] = zero16();
-    float m_run = -INFINITY, l_run = 0.f;
+    // l_run: sum of the fp32 probabilities (for LSE); w_run: sum of the bf16-rounded
+    // probabilities that feed the PV product (the output's normaliser).
+    float m_run = -INFINITY, l_run = 0.f, w_run = 0.f;
 
     for (int it = 0; it < cnt; ++it) {
         const int j = list[it];
@@ -127,17 +129,27 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
         const float m_new = fmaxf(m_run, mx);
         const float alpha = exp2f(m_run - m_new);
-        float rs = 0.f;
+        float rs = 0.f, ws = 0.f;
+        uint4 pb[2][2];  // bf16 probabilities, B operands of the PV product
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = exp2f(s[kt][r] * scale_log2 - m_new);
-                s[kt][r] = p;
-                rs += p;
+            for (int u = 0; u < 2; ++u) {
+                uint32_t w4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = exp2f(s[kt][8 * u + 2 * e] * scale_log2 - m_new);
+                    const float p1 = exp2f(s[kt][8 * u + 2 * e + 1] * scale_log2 - m_new);
+                    rs += p0 + p1;
+                    w4[e] = pack_bf16x2(p0, p1);
+                    ws += bf16_bits_to_f32(w4[e] & 0xffffu) + bf16_bits_to_f32(w4[e] >> 16);
+                }
+                pb[kt][u] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
             }
         rs += __shfl_xor(rs, 32);
+        ws += __shfl_xor(ws, 32);
         l_run = l_run * alpha + rs;
+        w_run = w_run * alpha + ws;
         m_run = m_new;
 #pragma unroll
         for (int t = 0; t < DT; ++t)
@@ -150,12 +162,7 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                uint4 pb;
-                pb.x = pack_bf16x2(s[kt][8 * u + 0], s[kt][8 * u + 1]);
-                pb.y = pack_bf16x2(s[kt][8 * u + 2], s[kt][8 * u + 3]);
-                pb.z = pack_bf16x2(s[kt][8 * u + 4], s[kt][8 * u + 5]);
-                pb.w = pack_bf16x2(s[kt][8 * u + 6], s[kt][8 * u + 7]);
-                const bf16x8_t b = as_bf16x8(pb);
+                const bf16x8_t b = as_bf16x8(pb[kt][u]);
                 const int key0 = 32 * kt + 16 * u + 4 * h;
 #pragma unroll
                 for (int t = 0; t < DT; ++t) {
@@ -171,35 +178,47 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
 
     // Epilogue: O[query][d] = O^T[d][query] / l. This lane holds query (wave*32 + c)
     // and d = 32t + 8g + 4h + e for register 4g + e of tile t.
-    const float inv_l = l_run > 0.f ? 1.0f / l_run : 0.f;
-    uint16_t* orow = o + head + (int64_t)qrow * D;
+    const float inv_l = w_run > 0.f ? 1.0f / w_run : 0.f;
+    if (o_fp32) {
+        float* orow = static_cast<float*>(o) + head + (int64_t)qrow * D;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            uint2 w;
-            w.x = pack_bf16x2(oacc[t][4 * g + 0] * inv_l, oacc[t][4 * g + 1] * inv_l);
-            w.y = pack_bf16x2(oacc[t][4 * g + 2] * inv_l, oacc[t][4 * g + 3] * inv_l);
-            *reinterpret_cast<uint2*>(orow + 32 * t + 8 * g + 4 * h) = w;
-        }
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4*>(orow + 32 * t + 8 * g + 4 * h) =
+                    make_float4(oacc[t][4 * g + 0] * inv_l, oacc[t][4 * g + 1] * inv_l,
+                                oacc[t][4 * g + 2] * inv_l, oacc[t][4 * g + 3] * inv_l);
+    } else {
+        uint16_t* orow = static_cast<uint16_t*>(o) + head + (int64_t)qrow * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint2 w;
+                w.x = pack_bf16x2(oacc[t][4 * g + 0] * inv_l, oacc[t][4 * g + 1] * inv_l);
+                w.y = pack_bf16x2(oacc[t][4 * g + 2] * inv_l, oacc[t][4 * g + 3] * inv_l);
+                *reinterpret_cast<uint2*>(orow + 32 * t + 8 * g + 4 * h) = w;
+            }
+    }
     if (lse && h == 0)
         lse[bh * (int64_t)S + qrow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t BH, int S, int D,
                            const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
-                           float softmax_scale, void* o, float* lse, hipStream_t stream) {
+                           float softmax_scale, void* o, bool o_fp32, float* lse,
+                           hipStream_t stream) {
     const int n = S / kBlockN;
     const unsigned grid = (unsigned)(BH * n);
     const float sl2 = softmax_scale * kLog2e;
     if (D == 128)
         attn_fwd_kernel<128><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, S, n, kv_count, kv_idx,
-            order, sl2, (uint16_t*)o, lse);
+            order, sl2, o, o_fp32 ? 1 : 0, lse);
     else
         attn_fwd_kernel<64><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, S, n, kv_count, kv_idx,
-            order, sl2, (uint16_t*)o, lse);
+            order, sl2, o, o_fp32 ? 1 : 0, lse);
     return hipGetLastError();
 }
 

@@ -34,10 +34,11 @@ hipError_t launch_lpt_order(const int32_t* counts, int64_t items, int n, int32_t
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t BH, int S, int D,
                            const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
-                           float softmax_scale, void* o, float* lse, hipStream_t stream);
+                           float softmax_scale, void* o, bool o_fp32, float* lse,
+                           hipStream_t stream);
 
-hipError_t launch_bwd_delta(const void* o, const void* d_o, int64_t rows, int D, float* delta,
-                            hipStream_t stream);
+hipError_t launch_bwd_delta(const void* o, bool o_fp32, const void* d_o, int64_t rows, int D,
+                            float* delta, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_o,
                            const float* lse, const float* delta, int64_t BH, int S, int D,
                            const int32_t* q_count, const int32_t* q_idx, const int32_t* order,

@@ -93,14 +93,15 @@ nabla_status_t nabla_build_mask(const void* q, const void* k, int32_t B, int32_t
 nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t B,
                                      int32_t H, int32_t S, int32_t D, int32_t N,
                                      const int32_t* kv_count, const int32_t* kv_idx,
-                                     float softmax_scale, void* o, float* lse, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     float softmax_scale, void* o, int32_t o_dtype, float* lse,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
     Shape s;
     nabla_status_t st = check_shape(B, H, S, D, N, &s);
     if (st != NABLA_OK) return st;
     if (!q || !k || !v || !o || !kv_count || !kv_idx) return NABLA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return NABLA_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || isinf(softmax_scale)) return NABLA_ERR_INVALID_ARG;
+    if (o_dtype != NABLA_DTYPE_BF16 && o_dtype != NABLA_DTYPE_FP32) return NABLA_ERR_INVALID_ARG;
     const FwdWorkspace w = fwd_workspace(s);
     if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
 
@@ -108,12 +109,12 @@ nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v
     hipStream_t hs = as_stream(stream);
     NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH * s.n, (int)s.n, order, hs));
     NABLA_LAUNCH(launch_attn_fwd(q, k, v, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx, order,
-                                 softmax_scale, o, lse, hs));
+                                 softmax_scale, o, o_dtype == NABLA_DTYPE_FP32, lse, hs));
     return NABLA_OK;
 }
 
 nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                     const void* d_o, const float* lse, int32_t B, int32_t H,
+                                     int32_t o_dtype, const void* d_o, const float* lse, int32_t B, int32_t H,
                                      int32_t S, int32_t D, int32_t N, const int32_t* kv_count,
                                      const int32_t* kv_idx, const int32_t* q_count,
                                      const int32_t* q_idx, float softmax_scale, void* dq,
@@ -129,6 +130,7 @@ nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v
     for (const void* p : ptrs)
         if (!aligned16(p)) return NABLA_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || isinf(softmax_scale)) return NABLA_ERR_INVALID_ARG;
+    if (o_dtype != NABLA_DTYPE_BF16 && o_dtype != NABLA_DTYPE_FP32) return NABLA_ERR_INVALID_ARG;
     const BwdWorkspace w = bwd_workspace(s);
     if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
 
@@ -136,7 +138,7 @@ nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v
     int32_t* order_q = reinterpret_cast<int32_t*>(ws_at(workspace, w.order_q));
     int32_t* order_kv = reinterpret_cast<int32_t*>(ws_at(workspace, w.order_kv));
     hipStream_t hs = as_stream(stream);
-    NABLA_LAUNCH(launch_bwd_delta(o, d_o, s.BH * s.S, (int)s.D, delta, hs));
+    NABLA_LAUNCH(launch_bwd_delta(o, o_dtype == NABLA_DTYPE_FP32, d_o, s.BH * s.S, (int)s.D, delta, hs));
     NABLA_LAUNCH(launch_lpt_order(q_count, s.BH * s.n, (int)s.n, order_kv, hs));
     NABLA_LAUNCH(launch_bwd_dkdv(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, q_count, q_idx,
                                  order_kv, softmax_scale, dk, dv, hs));

@@ -68,6 +68,9 @@ typedef struct {
 
 enum { NABLA_OP_MASK = 0, NABLA_OP_FWD = 1, NABLA_OP_BWD = 2 };
 
+/* Element type of the forward output O. */
+enum { NABLA_DTYPE_BF16 = 0, NABLA_DTYPE_FP32 = 1 };
+
 /* Bytes of device workspace the given operation needs (0 for invalid shapes). */
 NABLA_API size_t nabla_workspace_size(int32_t op, int32_t B, int32_t H, int32_t S, int32_t D, int32_t N);
 
@@ -100,16 +103,19 @@ NABLA_API nabla_status_t nabla_build_mask(const void* q, const void* k, int32_t 
  *   O_s   = sum_u softmax_u(scale * q_s . k_u) v_u over the keys u of the kept
  *           blocks kv_idx[b, h, i, 0 .. kv_count),
  *   LSE_s = log sum_u exp(scale * q_s . k_u)   (natural log).
- * o: bf16 [B, H, S, D] output. lse: fp32 [B, H, S] output, may be NULL (the
- * backward pass needs it). softmax_scale > 0, finite (the paper uses 1/sqrt(D)).
+ * o: [B, H, S, D] output of type o_dtype (NABLA_DTYPE_BF16 or NABLA_DTYPE_FP32;
+ * the arithmetic is the same, only the final store differs). lse: fp32 [B, H, S]
+ * output, may be NULL (the backward pass needs it). softmax_scale > 0, finite
+ * (the paper uses 1/sqrt(D)). The PV product uses the probabilities rounded to
+ * bf16 and divides by the sum of those rounded weights; LSE uses the fp32 sum.
  * Kept-block indices must lie in [0, n) and counts in [0, n]; a row with
  * count 0 yields O = 0 and LSE = -inf. bf16 MFMA, fp32 accumulation and softmax.
  */
 NABLA_API nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t B,
                                      int32_t H, int32_t S, int32_t D, int32_t N,
                                      const int32_t* kv_count, const int32_t* kv_idx,
-                                     float softmax_scale, void* o, float* lse, void* workspace,
-                                     size_t workspace_bytes, void* stream);
+                                     float softmax_scale, void* o, int32_t o_dtype, float* lse,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Block-sparse attention backward: gradients of the forward with the mask held
@@ -117,13 +123,13 @@ NABLA_API nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, con
  *   P = exp(scale * Q K^T - LSE) on kept blocks, Delta_s = dO_s . O_s,
  *   dV = P^T dO, dP = dO V^T, dS = P * (dP - Delta),
  *   dQ = scale * dS K, dK = scale * dS^T Q.
- * Inputs o and lse are the forward's outputs for the same q, k, v, lists and
- * scale; d_o is the output gradient (bf16). q_count/q_idx is the transpose of
+ * Inputs o (of type o_dtype, bf16 or fp32) and lse are the forward's outputs
+ * for the same q, k, v, lists and scale; d_o is the output gradient (bf16). q_count/q_idx is the transpose of
  * kv_count/kv_idx (as produced by nabla_build_mask). dq, dk, dv: bf16 outputs.
  * Deterministic: no atomics on the gradients.
  */
 NABLA_API nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                     const void* d_o, const float* lse, int32_t B, int32_t H,
+                                     int32_t o_dtype, const void* d_o, const float* lse, int32_t B, int32_t H,
                                      int32_t S, int32_t D, int32_t N, const int32_t* kv_count,
                                      const int32_t* kv_idx, const int32_t* q_count,
                                      const int32_t* q_idx, float softmax_scale, void* dq,

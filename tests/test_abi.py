@@ -106,8 +106,8 @@ def test_build_mask_sta_validation(lib):
 def test_fwd_validation(lib):
     f = lib.nabla_sparse_attn_fwd
 
-    def call(S=1024, D=64, scale=0.125, v=P, o=P, ws=P2, wsb=BIG):
-        return f(P, P, v, 1, 2, S, D, 64, P, P, scale, o, None, ws, wsb, None)
+    def call(S=1024, D=64, scale=0.125, v=P, o=P, odt=0, ws=P2, wsb=BIG):
+        return f(P, P, v, 1, 2, S, D, 64, P, P, scale, o, odt, None, ws, wsb, None)
 
     assert call(S=1000) == INVALID
     assert call(D=256) == UNSUPPORTED
@@ -116,6 +116,7 @@ def test_fwd_validation(lib):
     assert call(scale=float("inf")) == INVALID
     assert call(v=None) == INVALID
     assert call(o=None) == INVALID
+    assert call(odt=2) == INVALID
     assert call(ws=None) == WORKSPACE
     assert call(wsb=4) == WORKSPACE
 
@@ -123,13 +124,14 @@ def test_fwd_validation(lib):
 def test_bwd_validation(lib):
     f = lib.nabla_sparse_attn_bwd
 
-    def call(S=1024, lse=P, qc=P, scale=0.125, ws=P2, wsb=BIG):
-        return f(P, P, P, P, P, lse, 1, 2, S, 64, 64, P, P, qc, P, scale, P, P, P, ws, wsb, None)
+    def call(S=1024, lse=P, qc=P, scale=0.125, odt=0, ws=P2, wsb=BIG):
+        return f(P, P, P, P, odt, P, lse, 1, 2, S, 64, 64, P, P, qc, P, scale, P, P, P, ws, wsb, None)
 
     assert call(S=1000) == INVALID
     assert call(lse=None) == INVALID
     assert call(qc=None) == INVALID
     assert call(scale=-1.0) == INVALID
+    assert call(odt=5) == INVALID
     assert call(wsb=8) == WORKSPACE
 
 

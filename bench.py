@@ -1,0 +1,251 @@
+"""Benchmark of the NABLA hot path on one MI355X.
+
+One step = the whole forward hot path on the Wan 2.1 14B-like 720p layer
+(B=1, H=40, S=80640, D=128, N=64; 1260 blocks per head) at 90% block sparsity:
+    nabla_build_mask  (pool Q/K, reduced logits, CDF selection, compaction)
+    nabla_sparse_attn_fwd  (longest-first order + block-sparse flash forward)
+on inputs already resident in HBM. The metric is effective TFLOP/s on kept
+blocks: 4*N*N*D FLOP per kept (query block, key block) pair, divided by the
+step time. Also reported: the forward kernel's own TFLOP/s against the bf16
+MFMA peak (roofline), the speedup over the same kernel run dense, the mask
+stage's HBM GB/s, and the CPU oracle timed on a bounded sample of the same
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--sparsity S] [--no-cpu-baseline]
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s on kept blocks (% bf16 MFMA peak) + speedup vs dense at ~90% sparsity"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+FWD_KERNEL = "attn_fwd_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan14b_720p_traffic.json")
+FWD_SOURCE = os.path.join(ROOT, "block_sparse_attention_nabla_amd", "csrc", "attn_fwd.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_flops: float):
+    """HBM bytes per forward launch from committed rocprofv3 counters, if they
+    were taken on the current forward kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != source_hash(FWD_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, thr: float, lists_cpu, kept_per_block) -> dict:
+    """The oracle on a bounded sample: the mask of one head plus the forward of
+    sampled query blocks of that head, scaled to one head's full step."""
+    import numpy as np
+    import oracle
+
+    head = 0
+    q = x["q"].reshape(-1, w.S, w.D)[head:head + 1].float()
+    k = x["k"].reshape(-1, w.S, w.D)[head:head + 1].float()
+    v = x["v"].reshape(-1, w.S, w.D)[head:head + 1].float()
+    t0 = time.perf_counter()
+    m = oracle.build_mask(q, k, w.N, thr)
+    t_mask = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    nsamp = 48
+    blocks = sorted(rng.choice(w.n, nsamp, replace=False).tolist())
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, m["mask"], w.N, blocks=blocks)
+    t_fwd = time.perf_counter() - t0
+    kept_head = int(m["mask"].sum())
+    kept_sample = int(m["mask"][0, blocks].sum())
+    flops_per_kept = 4.0 * w.N * w.N * w.D
+    # One head's step: its full mask + the forward scaled from the sample.
+    t_head = t_mask + t_fwd * (kept_head / max(kept_sample, 1))
+    value = kept_head * flops_per_kept / t_head / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"head 0 of {w.B * w.H}: full mask ({t_mask:.2f} s) + forward of {nsamp} of "
+                       f"{w.n} query blocks ({kept_sample} kept blocks, {t_fwd:.2f} s), scaled to the "
+                       f"head's {kept_head} kept blocks; fp64 C + OpenMP"),
+            "seconds": round(t_mask + t_fwd, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b_720p")
+    ap.add_argument("--sparsity", type=float, default=0.90)
+    ap.add_argument("--dense-iters", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would be sharded across GPUs with no communication inside the path). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_sparse_attention_nabla_amd as nb
+    import synth
+
+    nb.load_library()
+    dev = torch.device("cuda:0")
+    w = synth.get_workload(args.workload)
+    thr = w.thr_for(args.sparsity)
+    log(f"workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D} n={w.n} thr={thr:.6f}")
+    t0 = time.time()
+    x = synth.make_inputs(w)
+    log(f"inputs generated on the host in {time.time() - t0:.1f} s")
+    q, k, v = (x[key].to(dev) for key in ("q", "k", "v"))
+    B, H, S, D, n = w.B, w.H, w.S, w.D, w.n
+
+    # Buffers and workspaces allocated once, outside the timed region.
+    lists = {"kv_count": torch.empty((B, H, n), dtype=torch.int32, device=dev),
+             "kv_idx": torch.empty((B, H, n, n), dtype=torch.int32, device=dev)}
+    ws_mask = torch.empty(nb.nabla_workspace_size(nb.NABLA_OP_MASK, B, H, S, D), dtype=torch.uint8, device=dev)
+    ws_fwd = torch.empty(nb.nabla_workspace_size(nb.NABLA_OP_FWD, B, H, S, D), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def mask_step():
+        nb.nabla_build_mask(q, k, thr, w.sta_struct(), out=lists, workspace=ws_mask, stream=stream)
+
+    def fwd_step():
+        nb.nabla_sparse_attn_fwd(q, k, v, lists["kv_count"], lists["kv_idx"], o=o, lse=lse,
+                                 workspace=ws_fwd, stream=stream)
+
+    for _ in range(args.warmup):
+        mask_step()
+        fwd_step()
+    torch.cuda.synchronize()
+    kept = int(lists["kv_count"].sum())
+    sparsity = 1.0 - kept / (B * H * n * n)
+    flops_per_kept = 4.0 * w.N * w.N * D
+    step_flops = kept * flops_per_kept
+    log(f"kept blocks {kept} -> sparsity {sparsity:.5f}; {step_flops / 1e12:.3f} TFLOP per step")
+
+    # Timed region: exactly K steps; HIP events on the launch stream bracket
+    # each stage so the forward kernel's own duration is known.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        mask_step()
+        ev[i][1].record(stream)
+        fwd_step()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    mask_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = step_flops / (fwd_ms * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms (mask {mask_ms:.3f} ms, forward {fwd_ms:.3f} ms); "
+        f"forward {fwd_tflops:.1f} TFLOP/s = {100 * fwd_tflops / PEAK_BF16_TFLOPS:.1f}% of peak")
+
+    # Mask stage algorithmic bytes: read Q and K once, write counts and lists.
+    mask_bytes = 2 * B * H * S * D * 2 + 4 * B * H * n + 4 * kept
+    mask_gbps = mask_bytes / (mask_ms * 1e-3) / 1e9
+
+    # Same kernel run dense: every block kept (thr >= 1).
+    if args.dense_iters < 1:
+        raise SystemExit("--dense-iters must be >= 1")
+    dense_lists = {"kv_count": torch.empty_like(lists["kv_count"]), "kv_idx": torch.empty_like(lists["kv_idx"])}
+    nb.nabla_build_mask(q, k, 1.0, out=dense_lists, workspace=ws_mask, stream=stream)
+    nb.nabla_sparse_attn_fwd(q, k, v, dense_lists["kv_count"], dense_lists["kv_idx"], o=o, lse=lse,
+                             workspace=ws_fwd, stream=stream)
+    torch.cuda.synchronize()
+    dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.dense_iters)]
+    for i in range(args.dense_iters):
+        dev_ev[i][0].record(stream)
+        nb.nabla_sparse_attn_fwd(q, k, v, dense_lists["kv_count"], dense_lists["kv_idx"], o=o, lse=lse,
+                                 workspace=ws_fwd, stream=stream)
+        dev_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dense_ms = sum(e[0].elapsed_time(e[1]) for e in dev_ev) / args.dense_iters
+    dense_flops = B * H * n * n * flops_per_kept
+    speedup = dense_ms / fwd_ms
+    log(f"dense forward {dense_ms:.2f} ms ({dense_flops / dense_ms / 1e9:.1f} TFLOP/s); "
+        f"speedup {speedup:.2f}x at density {1 - sparsity:.4f} (linearity {speedup * (1 - sparsity):.3f})")
+    del dense_lists
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "B": B, "H": H, "S": S, "D": D, "N": w.N,
+            "thr": round(thr, 6), "block_sparsity": round(sparsity, 5),
+            "step": "nabla_build_mask + nabla_sparse_attn_fwd (inputs resident in HBM)",
+        },
+        "pct_of_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "forward_tflops": round(fwd_tflops, 2),
+        "forward_ms": round(fwd_ms, 4),
+        "mask_ms": round(mask_ms, 4),
+        "mask_gbps": round(mask_gbps, 1),
+        "mask_pct_hbm_peak": round(100 * mask_gbps / PEAK_HBM_GBPS, 2),
+        "dense_forward_ms": round(dense_ms, 3),
+        "speedup_vs_dense_forward": round(speedup, 3),
+        "speedup_vs_dense_with_mask": round(dense_ms / (mask_ms + fwd_ms), 3),
+        "linearity": round(speedup * (1 - sparsity), 3),
+        "roofline": {
+            "kernel": FWD_KERNEL,
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(step_flops),
+            "algorithmic_flop_per_launch": step_flops,
+            "note": "forward call = one-workgroup longest-first ordering kernel + the attention kernel; "
+                    "events bracket both",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        xc = {key: x[key] for key in ("q", "k", "v")}
+        result["cpu_baseline"] = cpu_baseline(w, xc, thr, None, None)
+        log(f"cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -11,6 +11,9 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// Native 16-byte vector (HIP's uint4 is a wrapper struct that register
+// promotion does not always see through when held in arrays).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kBlockN = 64;  // tokens per block (N)

@@ -233,8 +233,8 @@ def main() -> int:
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(step_flops),
             "algorithmic_flop_per_launch": step_flops,
-            "note": "forward call = one-workgroup longest-first ordering kernel + the attention kernel; "
-                    "events bracket both",
+            "note": "forward call = per-head longest-first ordering kernel (one workgroup per head) + "
+                    "the attention kernel; events bracket both",
         },
         "cpu_baseline": None,
     }

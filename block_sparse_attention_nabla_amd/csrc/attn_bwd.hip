@@ -153,8 +153,8 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta, int S, int n,
     const int32_t* __restrict__ q_count, const int32_t* __restrict__ q_idx,
-    const int32_t* __restrict__ order, float scale, float scale_log2, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv) {
+    const int32_t* __restrict__ order, XcdSchedule sched, float scale, float scale_log2,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     constexpr int RST = BwdTile<D>::RST, TST = BwdTile<D>::TST;
     constexpr int KK = D / 16, DT = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t sQ[kBlockN * RST];
@@ -165,7 +165,8 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, c = lane & 31;
-    const int64_t item = order[blockIdx.x];
+    const int64_t item = scheduled_item(sched, order, blockIdx.x);
+    if (item < 0) return;  // padding slot (whole workgroup)
     const int64_t bh = item / n;
     const int kb = (int)(item % n);
     int cnt = q_count[item];
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(128) void dq_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta, int S, int n,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
-    const int32_t* __restrict__ order, float scale, float scale_log2, uint16_t* __restrict__ dq) {
+    const int32_t* __restrict__ order, XcdSchedule sched, float scale, float scale_log2,
+    uint16_t* __restrict__ dq) {
     constexpr int RST = BwdTile<D>::RST, TST = BwdTile<D>::TST;
     constexpr int KK = D / 16, DT = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t sK[kBlockN * RST];
@@ -255,7 +257,8 @@ __global__ __launch_bounds__(128) void dq_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, c = lane & 31;
-    const int64_t item = order[blockIdx.x];
+    const int64_t item = scheduled_item(sched, order, blockIdx.x);
+    if (item < 0) return;  // padding slot (whole workgroup)
     const int64_t bh = item / n;
     const int qb = (int)(item % n);
     int cnt = kv_count[item];
@@ -333,36 +336,40 @@ hipError_t launch_bwd_delta(const void* o, bool o_fp32, const void* d_o, int64_t
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_o,
                            const float* lse, const float* delta, int64_t BH, int S, int D,
                            const int32_t* q_count, const int32_t* q_idx, const int32_t* order,
-                           float softmax_scale, void* dk, void* dv, hipStream_t stream) {
+                           const XcdSchedule& sched, float softmax_scale, void* dk, void* dv,
+                           hipStream_t stream) {
     const int n = S / kBlockN;
-    const unsigned grid = (unsigned)(BH * n);
+    const unsigned grid = (unsigned)sched.grid;
     const float sl2 = softmax_scale * kLog2e;
     if (D == 128)
         dkdv_kernel<128><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse,
-            delta, S, n, q_count, q_idx, order, softmax_scale, sl2, (uint16_t*)dk, (uint16_t*)dv);
+            delta, S, n, q_count, q_idx, order, sched, softmax_scale, sl2, (uint16_t*)dk,
+            (uint16_t*)dv);
     else
         dkdv_kernel<64><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse,
-            delta, S, n, q_count, q_idx, order, softmax_scale, sl2, (uint16_t*)dk, (uint16_t*)dv);
+            delta, S, n, q_count, q_idx, order, sched, softmax_scale, sl2, (uint16_t*)dk,
+            (uint16_t*)dv);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* d_o,
                          const float* lse, const float* delta, int64_t BH, int S, int D,
                          const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
-                         float softmax_scale, void* dq, hipStream_t stream) {
+                         const XcdSchedule& sched, float softmax_scale, void* dq,
+                         hipStream_t stream) {
     const int n = S / kBlockN;
-    const unsigned grid = (unsigned)(BH * n);
+    const unsigned grid = (unsigned)sched.grid;
     const float sl2 = softmax_scale * kLog2e;
     if (D == 128)
         dq_kernel<128><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse,
-            delta, S, n, kv_count, kv_idx, order, softmax_scale, sl2, (uint16_t*)dq);
+            delta, S, n, kv_count, kv_idx, order, sched, softmax_scale, sl2, (uint16_t*)dq);
     else
         dq_kernel<64><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse,
-            delta, S, n, kv_count, kv_idx, order, softmax_scale, sl2, (uint16_t*)dq);
+            delta, S, n, kv_count, kv_idx, order, sched, softmax_scale, sl2, (uint16_t*)dq);
     return hipGetLastError();
 }
 

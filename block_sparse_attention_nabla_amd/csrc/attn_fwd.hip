@@ -45,8 +45,8 @@ template <int D>
 __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int S, int n, const int32_t* __restrict__ kv_count,
-    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ order, float scale_log2,
-    void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
+    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ order, XcdSchedule sched,
+    float scale_log2, void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
     using T = Tile<D>;
     constexpr int KK = D / 16;  // MFMA k-steps over the head dimension
     constexpr int DT = D / 32;  // 32-row d tiles of O^T
@@ -57,7 +57,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, c = lane & 31;
-    const int64_t item = order[blockIdx.x];
+    const int64_t item = scheduled_item(sched, order, blockIdx.x);
+    if (item < 0) return;  // padding slot (whole workgroup)
     const int64_t bh = item / n;
     const int qb = (int)(item % n);
     int cnt = kv_count[item];
@@ -238,19 +239,19 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t BH, int S, int D,
                            const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
-                           float softmax_scale, void* o, bool o_fp32, float* lse,
-                           hipStream_t stream) {
+                           const XcdSchedule& sched, float softmax_scale, void* o, bool o_fp32,
+                           float* lse, hipStream_t stream) {
     const int n = S / kBlockN;
-    const unsigned grid = (unsigned)(BH * n);
+    const unsigned grid = (unsigned)sched.grid;
     const float sl2 = softmax_scale * kLog2e;
     if (D == 128)
         attn_fwd_kernel<128><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, S, n, kv_count, kv_idx,
-            order, sl2, o, o_fp32 ? 1 : 0, lse);
+            order, sched, sl2, o, o_fp32 ? 1 : 0, lse);
     else
         attn_fwd_kernel<64><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, S, n, kv_count, kv_idx,
-            order, sl2, o, o_fp32 ? 1 : 0, lse);
+            order, sched, sl2, o, o_fp32 ? 1 : 0, lse);
     return hipGetLastError();
 }
 

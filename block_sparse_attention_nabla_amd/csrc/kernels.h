@@ -27,13 +27,39 @@ hipError_t launch_select(const float* logits, int64_t BH, int n, int keep_all, u
 hipError_t launch_transpose(const uint32_t* bits, int64_t BH, int n, int words_per_row,
                             int32_t* q_count, int32_t* q_idx, hipStream_t stream);
 
-// Longest-first work order: order[0 .. BH*n) = item ids (bh*n + i) sorted by
-// counts[item] descending (ties in any order).
-hipError_t launch_lpt_order(const int32_t* counts, int64_t items, int n, int32_t* order,
+// Per-head longest-first order: order[h*n + p] = item id (h*n + i) of head h's
+// p-th item, counts descending (ties in any order).
+hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int n, int32_t* order,
                             hipStream_t stream);
+
+// XCD-aware launch geometry (see schedule.hip): heads are split into `parts`
+// interleaved shares so that `units` = BH * parts is a multiple of the 8 XCDs;
+// workgroup b runs on XCD b % 8 and serves unit x + 8 * (m / cap), position
+// m % cap, with x = b % 8, m = b / 8.
+struct XcdSchedule {
+    int parts;
+    int64_t units;
+    int cap;
+    int n;
+    int64_t grid;
+};
+XcdSchedule make_schedule(int64_t BH, int n);
+
+// Work item of workgroup b, or -1 for a padding slot.
+__device__ __forceinline__ int64_t scheduled_item(const XcdSchedule& s, const int32_t* order,
+                                                  int64_t b) {
+    const int64_t x = b % 8, m = b / 8;
+    const int64_t unit = x + 8 * (m / s.cap);
+    const int64_t head = unit / s.parts;
+    const int part = (int)(unit % s.parts);
+    const int64_t pos = part + (int64_t)s.parts * (m % s.cap);
+    if (pos >= s.n) return -1;
+    return order[head * s.n + pos];
+}
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t BH, int S, int D,
                            const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
+                           const XcdSchedule& sched,
                            float softmax_scale, void* o, bool o_fp32, float* lse,
                            hipStream_t stream);
 
@@ -42,10 +68,12 @@ hipError_t launch_bwd_delta(const void* o, bool o_fp32, const void* d_o, int64_t
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* d_o,
                            const float* lse, const float* delta, int64_t BH, int S, int D,
                            const int32_t* q_count, const int32_t* q_idx, const int32_t* order,
-                           float softmax_scale, void* dk, void* dv, hipStream_t stream);
+                           const XcdSchedule& sched, float softmax_scale, void* dk, void* dv,
+                           hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* d_o,
                          const float* lse, const float* delta, int64_t BH, int S, int D,
                          const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
-                         float softmax_scale, void* dq, hipStream_t stream);
+                         const XcdSchedule& sched, float softmax_scale, void* dq,
+                         hipStream_t stream);
 
 }  // namespace nabla

@@ -107,8 +107,9 @@ nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v
 
     int32_t* order = reinterpret_cast<int32_t*>(ws_at(workspace, w.order));
     hipStream_t hs = as_stream(stream);
-    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH * s.n, (int)s.n, order, hs));
-    NABLA_LAUNCH(launch_attn_fwd(q, k, v, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx, order,
+    const XcdSchedule sched = make_schedule(s.BH, (int)s.n);
+    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, (int)s.n, order, hs));
+    NABLA_LAUNCH(launch_attn_fwd(q, k, v, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx, order, sched,
                                  softmax_scale, o, o_dtype == NABLA_DTYPE_FP32, lse, hs));
     return NABLA_OK;
 }
@@ -139,12 +140,13 @@ nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v
     int32_t* order_kv = reinterpret_cast<int32_t*>(ws_at(workspace, w.order_kv));
     hipStream_t hs = as_stream(stream);
     NABLA_LAUNCH(launch_bwd_delta(o, o_dtype == NABLA_DTYPE_FP32, d_o, s.BH * s.S, (int)s.D, delta, hs));
-    NABLA_LAUNCH(launch_lpt_order(q_count, s.BH * s.n, (int)s.n, order_kv, hs));
+    const XcdSchedule sched = make_schedule(s.BH, (int)s.n);
+    NABLA_LAUNCH(launch_lpt_order(q_count, s.BH, (int)s.n, order_kv, hs));
     NABLA_LAUNCH(launch_bwd_dkdv(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, q_count, q_idx,
-                                 order_kv, softmax_scale, dk, dv, hs));
-    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH * s.n, (int)s.n, order_q, hs));
+                                 order_kv, sched, softmax_scale, dk, dv, hs));
+    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, (int)s.n, order_q, hs));
     NABLA_LAUNCH(launch_bwd_dq(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx,
-                               order_q, softmax_scale, dq, hs));
+                               order_q, sched, softmax_scale, dq, hs));
     return NABLA_OK;
 }
 

@@ -1,10 +1,17 @@
-// schedule.hip -- longest-processing-time-first order of attention work items.
+// schedule.hip -- order of attention work items (query or key blocks).
 //
-// Kept-block counts differ a lot between query blocks (the CDF rule keeps few
-// blocks for peaked rows and many for flat ones, and the STA union adds a
-// border-dependent number). Launching the items with the most kept blocks
-// first lets the hardware dispatcher fill the tail with short items.
-// Counting sort over counts 0..n in one workgroup (LDS histogram + scan).
+// Two goals. (1) Cache locality: every kept block pair re-reads a 32 KB K/V
+// tile pair, and one head's K and V (41 MB at 80640 x 128) is re-read about a
+// hundred times, so the items that run at the same time should belong to
+// as few heads as possible -- and, since each of MI355X's 8 XCDs has its own
+// L2, the items one XCD runs should come from the same head. Workgroup b of
+// a launch runs on XCD b % 8 (round-robin dispatch), so the launch maps
+// workgroup b to a (head part, position) pair: XCD x walks the parts
+// x, x + 8, x + 16, ... and each part is one head (or an interleaved share of
+// one, when the head count is not a multiple of 8).
+// (2) Load balance: kept-block counts differ a lot between query blocks (the
+// CDF rule keeps few blocks for peaked rows and many for flat ones), so
+// within a head the longest items start first.
 
 #include "common.h"
 #include "kernels.h"
@@ -13,55 +20,74 @@ namespace nabla {
 
 constexpr int kLptThreads = 1024;
 
-__global__ __launch_bounds__(kLptThreads) void lpt_order_kernel(const int32_t* __restrict__ counts,
-                                                                 int64_t items, int n,
-                                                                 int32_t* __restrict__ order) {
+// One workgroup per head: counting sort of the head's n items by count
+// (descending). order[h*n + p] = global item id of the head's p-th item.
+__global__ __launch_bounds__(kLptThreads) void head_lpt_kernel(const int32_t* __restrict__ counts,
+                                                               int n,
+                                                               int32_t* __restrict__ order) {
     __shared__ int hist[NABLA_MAX_BLOCKS + 1];
     __shared__ int chunk_sum[kLptThreads];
     const int t = threadIdx.x;
+    const int64_t base = (int64_t)blockIdx.x * n;
     const int nb = n + 1;  // count values 0..n
     for (int c = t; c < nb; c += kLptThreads) hist[c] = 0;
     __syncthreads();
-    for (int64_t it = t; it < items; it += kLptThreads) {
-        int c = counts[it];
+    for (int it = t; it < n; it += kLptThreads) {
+        int c = counts[base + it];
         c = c < 0 ? 0 : (c > n ? n : c);
         atomicAdd(&hist[c], 1);
     }
     __syncthreads();
-    // Exclusive scan in descending count order: slot position r = n - c.
-    // Thread t owns a contiguous range of ranks [t*per, (t+1)*per).
+    // Exclusive scan in descending count order: rank r <-> count n - r.
+    // Thread t owns the contiguous ranks [t*per, (t+1)*per).
     const int per = (nb + kLptThreads - 1) / kLptThreads;
     int local = 0;
     for (int r = t * per; r < (t + 1) * per && r < nb; ++r) local += hist[n - r];
     chunk_sum[t] = local;
     __syncthreads();
-    // Hillis-Steele inclusive scan over the 1024 chunk sums.
-    for (int off = 1; off < kLptThreads; off <<= 1) {
+    for (int off = 1; off < kLptThreads; off <<= 1) {  // inclusive scan of the chunk sums
         const int add = t >= off ? chunk_sum[t - off] : 0;
         __syncthreads();
         chunk_sum[t] += add;
         __syncthreads();
     }
-    int run = chunk_sum[t] - local;  // exclusive prefix of this thread's range
+    int run = chunk_sum[t] - local;
     for (int r = t * per; r < (t + 1) * per && r < nb; ++r) {
         const int c = n - r;
         const int hc = hist[c];
-        hist[c] = run;  // becomes the next free slot of count c
+        hist[c] = run;  // next free position of count c
         run += hc;
     }
     __syncthreads();
-    for (int64_t it = t; it < items; it += kLptThreads) {
-        int c = counts[it];
+    for (int it = t; it < n; it += kLptThreads) {
+        int c = counts[base + it];
         c = c < 0 ? 0 : (c > n ? n : c);
         const int pos = atomicAdd(&hist[c], 1);
-        order[pos] = (int32_t)it;
+        order[base + pos] = (int32_t)(base + it);
     }
 }
 
-hipError_t launch_lpt_order(const int32_t* counts, int64_t items, int n, int32_t* order,
+hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int n, int32_t* order,
                             hipStream_t stream) {
-    lpt_order_kernel<<<1, kLptThreads, 0, stream>>>(counts, items, n, order);
+    head_lpt_kernel<<<(unsigned)BH, kLptThreads, 0, stream>>>(counts, n, order);
     return hipGetLastError();
+}
+
+XcdSchedule make_schedule(int64_t BH, int n) {
+    int64_t a = BH, b = 8;  // gcd(BH, 8)
+    while (b != 0) {
+        const int64_t r = a % b;
+        a = b;
+        b = r;
+    }
+    const int g = (int)a;
+    XcdSchedule s;
+    s.parts = 8 / g;                         // parts per head
+    s.units = BH * s.parts;                  // a multiple of 8
+    s.cap = (n + s.parts - 1) / s.parts;     // positions per part
+    s.n = n;
+    s.grid = s.units * s.cap;
+    return s;
 }
 
 }  // namespace nabla

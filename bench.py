@@ -14,6 +14,16 @@ workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--sparsity S] [--no-cpu-baseline]
 Prints ONE JSON line on stdout; progress goes to stderr.
+
+HBM traffic of the forward kernel (roofline "traffic"): run twice under
+rocprofv3 with the counters FETCH_SIZE and WRITE_SIZE,
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o fetch -- \
+        python bench.py --steps 1 --warmup 1 --no-dense --no-cpu-baseline --traffic-calibration
+(and the same with WRITE_SIZE), then
+    python bench.py --summarize-traffic DIR/fetch_counter_collection.csv DIR/write_counter_collection.csv
+which scales each counter by what it reads for a plain 1 GiB copy kernel run
+in the same process and records the result, keyed to the forward kernel's
+source, for later bench runs.
 """
 
 from __future__ import annotations
@@ -59,7 +69,51 @@ def measured_traffic(launch_flops: float):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x, thr: float, lists_cpu, kept_per_block) -> dict:
+CALIB_BYTES = 1 << 30  # copy-kernel calibration: read and write 1 GiB
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str) -> dict:
+    """Per-launch HBM bytes of the forward kernel from two rocprofv3 counter CSVs."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {"fwd": [], "copy": []}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            kb = float(r["Counter_Value"])
+            if FWD_KERNEL in r["Kernel_Name"]:
+                out["fwd"].append(kb)
+            elif "elementwise" in r["Kernel_Name"] and int(r["Grid_Size"]) > (1 << 20):
+                out["copy"].append(kb)
+        return out
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    wr = per_kernel(write_csv, "WRITE_SIZE")
+    if not (f["fwd"] and f["copy"] and wr["fwd"] and wr["copy"]):
+        raise SystemExit("counter CSVs lack forward or calibration-copy dispatches")
+    f_scale = (CALIB_BYTES / 1024.0) / max(f["copy"])
+    w_scale = (CALIB_BYTES / 1024.0) / max(wr["copy"])
+    fetch_b = sum(f["fwd"]) / len(f["fwd"]) * 1024.0 * f_scale
+    write_b = sum(wr["fwd"]) / len(wr["fwd"]) * 1024.0 * w_scale
+    res = {
+        "kernel": FWD_KERNEL,
+        "workload": "wan14b_720p at 90% block sparsity",
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "bytes_per_launch": fetch_b + write_b,
+        "calibration": {"copy_bytes": CALIB_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
+                        "raw_copy_fetch_kb": max(f["copy"]), "raw_copy_write_kb": max(wr["copy"])},
+        "launches": {"fetch": len(f["fwd"]), "write": len(wr["fwd"])},
+        "kernel_source_sha256_16": source_hash(FWD_SOURCE),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(res, fh, indent=2)
+    return res
+
+
+def cpu_baseline(w, x, thr: float) -> dict:
     """The oracle on a bounded sample: the mask of one head plus the forward of
     sampled query blocks of that head, scaled to one head's full step."""
     import numpy as np
@@ -100,7 +154,14 @@ def main() -> int:
     ap.add_argument("--sparsity", type=float, default=0.90)
     ap.add_argument("--dense-iters", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense comparison run")
+    ap.add_argument("--traffic-calibration", action="store_true",
+                    help="also run a plain 1 GiB copy kernel (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.summarize_traffic:
+        print(json.dumps(summarize_traffic(*args.summarize_traffic)))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(heads would be sharded across GPUs with no communication inside the path). "
@@ -174,27 +235,37 @@ def main() -> int:
     mask_gbps = mask_bytes / (mask_ms * 1e-3) / 1e9
 
     # Same kernel run dense: every block kept (thr >= 1).
-    if args.dense_iters < 1:
-        raise SystemExit("--dense-iters must be >= 1")
-    dense_lists = {"kv_count": torch.empty_like(lists["kv_count"]), "kv_idx": torch.empty_like(lists["kv_idx"])}
-    nb.nabla_build_mask(q, k, 1.0, out=dense_lists, workspace=ws_mask, stream=stream)
-    nb.nabla_sparse_attn_fwd(q, k, v, dense_lists["kv_count"], dense_lists["kv_idx"], o=o, lse=lse,
-                             workspace=ws_fwd, stream=stream)
-    torch.cuda.synchronize()
-    dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.dense_iters)]
-    for i in range(args.dense_iters):
-        dev_ev[i][0].record(stream)
+    if args.no_dense:
+        args.dense_iters = 0
+    dense_ms = float("nan")
+    if args.dense_iters > 0:
+        dense_lists = {"kv_count": torch.empty_like(lists["kv_count"]), "kv_idx": torch.empty_like(lists["kv_idx"])}
+        nb.nabla_build_mask(q, k, 1.0, out=dense_lists, workspace=ws_mask, stream=stream)
         nb.nabla_sparse_attn_fwd(q, k, v, dense_lists["kv_count"], dense_lists["kv_idx"], o=o, lse=lse,
                                  workspace=ws_fwd, stream=stream)
-        dev_ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dense_ms = sum(e[0].elapsed_time(e[1]) for e in dev_ev) / args.dense_iters
-    dense_flops = B * H * n * n * flops_per_kept
-    speedup = dense_ms / fwd_ms
-    log(f"dense forward {dense_ms:.2f} ms ({dense_flops / dense_ms / 1e9:.1f} TFLOP/s); "
-        f"speedup {speedup:.2f}x at density {1 - sparsity:.4f} (linearity {speedup * (1 - sparsity):.3f})")
-    del dense_lists
+        torch.cuda.synchronize()
+        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.dense_iters)]
+        for i in range(args.dense_iters):
+            dev_ev[i][0].record(stream)
+            nb.nabla_sparse_attn_fwd(q, k, v, dense_lists["kv_count"], dense_lists["kv_idx"], o=o, lse=lse,
+                                     workspace=ws_fwd, stream=stream)
+            dev_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        dense_ms = sum(e[0].elapsed_time(e[1]) for e in dev_ev) / args.dense_iters
+        dense_flops = B * H * n * n * flops_per_kept
+        speedup = dense_ms / fwd_ms
+        log(f"dense forward {dense_ms:.2f} ms ({dense_flops / dense_ms / 1e9:.1f} TFLOP/s); "
+            f"speedup {speedup:.2f}x at density {1 - sparsity:.4f} (linearity {speedup * (1 - sparsity):.3f})")
+        del dense_lists
 
+    if args.traffic_calibration:
+        xa = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
+        ya = torch.empty_like(xa)
+        torch.mul(xa, 1.0, out=ya)  # plain copy kernel: reads and writes 1 GiB
+        torch.cuda.synchronize()
+        del xa, ya
+
+    speedup = dense_ms / fwd_ms
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -220,10 +291,11 @@ def main() -> int:
         "mask_ms": round(mask_ms, 4),
         "mask_gbps": round(mask_gbps, 1),
         "mask_pct_hbm_peak": round(100 * mask_gbps / PEAK_HBM_GBPS, 2),
-        "dense_forward_ms": round(dense_ms, 3),
-        "speedup_vs_dense_forward": round(speedup, 3),
-        "speedup_vs_dense_with_mask": round(dense_ms / (mask_ms + fwd_ms), 3),
-        "linearity": round(speedup * (1 - sparsity), 3),
+        "dense_forward_ms": round(dense_ms, 3) if args.dense_iters > 0 else None,
+        "speedup_vs_dense_forward": round(speedup, 3) if args.dense_iters > 0 else None,
+        "speedup_vs_dense_with_mask": (round(dense_ms / (mask_ms + fwd_ms), 3)
+                                       if args.dense_iters > 0 else None),
+        "linearity": round(speedup * (1 - sparsity), 3) if args.dense_iters > 0 else None,
         "roofline": {
             "kernel": FWD_KERNEL,
             "bound": "mfma",
@@ -241,7 +313,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         xc = {key: x[key] for key in ("q", "k", "v")}
-        result["cpu_baseline"] = cpu_baseline(w, xc, thr, None, None)
+        result["cpu_baseline"] = cpu_baseline(w, xc, thr)
         log(f"cpu baseline {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
     return 0

@@ -7,8 +7,8 @@
 // L2, the items one XCD runs should come from the same head. Workgroup b of
 // a launch runs on XCD b % 8 (round-robin dispatch), so the launch maps
 // workgroup b to a (head part, position) pair: XCD x walks the parts
-// x, x + 8, x + 16, ... and each part is one head (or an interleaved share of
-// one, when the head count is not a multiple of 8).
+// x, x + 8, x + 16, ...; a part is an interleaved share of one head (every
+// second, fourth or eighth item of its longest-first order).
 // (2) Load balance: kept-block counts differ a lot between query blocks (the
 // CDF rule keeps few blocks for peaked rows and many for flat ones), so
 // within a head the longest items start first.
@@ -82,7 +82,10 @@ XcdSchedule make_schedule(int64_t BH, int n) {
     }
     const int g = (int)a;
     XcdSchedule s;
-    s.parts = 8 / g;                         // parts per head
+    // Parts per head: at least 2, so that two XCDs share each head and at most
+    // four heads' K/V (4 x 41 MB at 80640 x 128) are live at once -- they fit
+    // the 256 MB Infinity Cache, which eight live heads would overflow.
+    s.parts = 8 / g < 2 ? 2 : 8 / g;
     s.units = BH * s.parts;                  // a multiple of 8
     s.cap = (n + s.parts - 1) / s.parts;     // positions per part
     s.n = n;

@@ -113,36 +113,99 @@ def summarize_traffic(fetch_csv: str, write_csv: str) -> dict:
     return res
 
 
-def cpu_baseline(w, x, thr: float) -> dict:
-    """The oracle on a bounded sample: the mask of one head plus the forward of
-    sampled query blocks of that head, scaled to one head's full step."""
-    import numpy as np
+def cpu_baseline(w, x, thr: float, heads: int = 2) -> dict:
+    """The oracle on a bounded sample of the same workload: the whole hot path
+    (mask, then the masked forward over every query block) for the first
+    `heads` heads; the rate is kept-block FLOP of the sample over its time."""
     import oracle
 
-    head = 0
-    q = x["q"].reshape(-1, w.S, w.D)[head:head + 1].float()
-    k = x["k"].reshape(-1, w.S, w.D)[head:head + 1].float()
-    v = x["v"].reshape(-1, w.S, w.D)[head:head + 1].float()
+    q = x["q"].reshape(-1, w.S, w.D)[:heads].float()
+    k = x["k"].reshape(-1, w.S, w.D)[:heads].float()
+    v = x["v"].reshape(-1, w.S, w.D)[:heads].float()
     t0 = time.perf_counter()
     m = oracle.build_mask(q, k, w.N, thr)
     t_mask = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    nsamp = 48
-    blocks = sorted(rng.choice(w.n, nsamp, replace=False).tolist())
     t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, m["mask"], w.N, blocks=blocks)
+    oracle.attn_fwd(q, k, v, m["mask"], w.N)
     t_fwd = time.perf_counter() - t0
-    kept_head = int(m["mask"].sum())
-    kept_sample = int(m["mask"][0, blocks].sum())
-    flops_per_kept = 4.0 * w.N * w.N * w.D
-    # One head's step: its full mask + the forward scaled from the sample.
-    t_head = t_mask + t_fwd * (kept_head / max(kept_sample, 1))
-    value = kept_head * flops_per_kept / t_head / 1e12
-    return {"value": value, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": (f"head 0 of {w.B * w.H}: full mask ({t_mask:.2f} s) + forward of {nsamp} of "
-                       f"{w.n} query blocks ({kept_sample} kept blocks, {t_fwd:.2f} s), scaled to the "
-                       f"head's {kept_head} kept blocks; fp64 C + OpenMP"),
+    kept = int(m["mask"].sum())
+    flops = kept * 4.0 * w.N * w.N * w.D
+    return {"value": flops / (t_mask + t_fwd) / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"heads 0..{heads - 1} of {w.B * w.H}: mask ({t_mask:.1f} s) and forward over all "
+                       f"{w.n} query blocks per head ({kept} kept blocks, {t_fwd:.1f} s); "
+                       f"fp64 C + OpenMP"),
             "seconds": round(t_mask + t_fwd, 2)}
+
+
+def train_step(args, dev, stream) -> dict:
+    """Mask + forward + backward on the 2B-DiT training shape (B=2, H=16, S=61440,
+    D=128; ~85% block sparsity). Every step rebuilds the mask from fresh Q/K
+    (generated on the GPU from the same recipe, one seed per step)."""
+    import torch
+    import block_sparse_attention_nabla_amd as nb
+    import synth
+
+    w = synth.get_workload("dit2b_train")
+    thr = w.thr_for(0.85)
+    B, H, S, D, n = w.B, w.H, w.S, w.D, w.n
+    steps = max(1, args.train_steps)
+    t0 = time.time()
+    sets = [synth.make_inputs(w, step=s + 1, device=dev) for s in range(steps + 1)]
+    d_o = synth.make_dout(w, device=dev)
+    log(f"train: {steps + 1} fresh input sets generated on the GPU in {time.time() - t0:.1f} s")
+    lists = {"kv_count": torch.empty((B, H, n), dtype=torch.int32, device=dev),
+             "kv_idx": torch.empty((B, H, n, n), dtype=torch.int32, device=dev),
+             "q_count": torch.empty((B, H, n), dtype=torch.int32, device=dev),
+             "q_idx": torch.empty((B, H, n, n), dtype=torch.int32, device=dev)}
+    ws = {op: torch.empty(nb.nabla_workspace_size(op, B, H, S, D), dtype=torch.uint8, device=dev)
+          for op in (nb.NABLA_OP_MASK, nb.NABLA_OP_FWD, nb.NABLA_OP_BWD)}
+    o = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(o) for _ in range(3))
+
+    def one(x, ev=None):
+        if ev: ev[0].record(stream)
+        nb.nabla_build_mask(x["q"], x["k"], thr, transpose=True, out=lists,
+                            workspace=ws[nb.NABLA_OP_MASK], stream=stream)
+        if ev: ev[1].record(stream)
+        nb.nabla_sparse_attn_fwd(x["q"], x["k"], x["v"], lists["kv_count"], lists["kv_idx"], o=o,
+                                 lse=lse, workspace=ws[nb.NABLA_OP_FWD], stream=stream)
+        if ev: ev[2].record(stream)
+        nb.nabla_sparse_attn_bwd(x["q"], x["k"], x["v"], o, d_o, lse, lists["kv_count"],
+                                 lists["kv_idx"], lists["q_count"], lists["q_idx"], dq=dq, dk=dk,
+                                 dv=dv, workspace=ws[nb.NABLA_OP_BWD], stream=stream)
+        if ev: ev[3].record(stream)
+
+    one(sets[0])  # warm-up
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    kept = []
+    t_start = time.perf_counter()
+    for i in range(steps):
+        one(sets[i + 1], evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t_start) * 1e3 / steps
+    kept_last = int(lists["kv_count"].sum())
+    mask_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    fpk = 4.0 * w.N * w.N * D
+    res = {
+        "workload": f"{w.name}: {w.description}",
+        "thr": round(thr, 6),
+        "block_sparsity_last_step": round(1.0 - kept_last / (B * H * n * n), 5),
+        "ms_per_step": round(wall, 3),
+        "mask_ms": round(mask_ms, 3),
+        "forward_ms": round(fwd_ms, 3),
+        "backward_ms": round(bwd_ms, 3),
+        "forward_tflops": round(kept_last * fpk / (fwd_ms * 1e-3) / 1e12, 1),
+        "backward_tflops": round(2.5 * kept_last * fpk / (bwd_ms * 1e-3) / 1e12, 1),
+        "step_tflops": round(3.5 * kept_last * fpk / (wall * 1e-3) / 1e12, 1),
+        "flop_model": "forward 4*N*N*D, backward 10*N*N*D per kept block pair",
+    }
+    log(f"train: {res}")
+    return res
 
 
 def main() -> int:
@@ -158,6 +221,9 @@ def main() -> int:
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="also run a plain 1 GiB copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training-step figures (2B-DiT shape, forward + backward)")
+    ap.add_argument("--train-steps", type=int, default=4)
     args = ap.parse_args()
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic)))
@@ -310,6 +376,10 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if not args.no_train:
+        del o, lse, lists, ws_mask, ws_fwd, q, k, v
+        torch.cuda.empty_cache()
+        result["train_step"] = train_step(args, dev, stream)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         xc = {key: x[key] for key in ("q", "k", "v")}

@@ -230,3 +230,38 @@ def attn_bwd(q, k, v, dout, mask: np.ndarray, N: int, scale: Optional[float] = N
     lib.nabla_oracle_attn_bwd_dkdv(q, k, v, dout, BH, S, D, N, m, sc,
                                    arr2.ctypes.data if arr2 is not None else None, cnt2, dk, dv)
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# Token reordering, section 3.1.1 (Figure 3): "fractal flattening". Each P x P
+# spatial patch of a frame becomes P*P consecutive tokens; frames keep their
+# time order. Raster order is (t, y, x) with x fastest.
+# ----------------------------------------------------------------------------
+def token_order(T: int, Hs: int, Ws: int, P: int) -> np.ndarray:
+    """perm[s] = raster index of the token at block-order position s."""
+    if Hs % P or Ws % P:
+        raise ValueError("frame height and width must be multiples of P")
+    tH, tW = Hs // P, Ws // P
+    perm = np.empty(T * Hs * Ws, dtype=np.int64)
+    s = 0
+    for t in range(T):
+        for ty in range(tH):
+            for tx in range(tW):
+                for py in range(P):
+                    for px in range(P):
+                        y, x = ty * P + py, tx * P + px
+                        perm[s] = (t * Hs + y) * Ws + x
+                        s += 1
+    return perm
+
+
+def tokens_to_blocks(x: np.ndarray, T: int, Hs: int, Ws: int, P: int) -> np.ndarray:
+    """Rows of x (axis -2: tokens in raster order) into block order."""
+    return np.ascontiguousarray(x[..., token_order(T, Hs, Ws, P), :])
+
+
+def blocks_to_tokens(x: np.ndarray, T: int, Hs: int, Ws: int, P: int) -> np.ndarray:
+    """Inverse of tokens_to_blocks: rows in block order back to raster order."""
+    out = np.empty_like(x)
+    out[..., token_order(T, Hs, Ws, P), :] = x
+    return out

@@ -55,3 +55,12 @@ def test_gaussian_taps():
     assert t.numel() == 17
     assert abs(float(t.sum()) - 1.0) < 1e-12
     assert torch.equal(t, t.flip(0))
+
+
+def test_generator_block_order_matches_the_oracle_reordering():
+    # The generator emits tokens in block order; its permutation and the oracle's
+    # reordering are written independently and must agree (section 3.1.1).
+    import oracle
+    for T, Hs, Ws, P in ((1, 16, 16, 8), (3, 24, 40, 8), (2, 6, 10, 2)):
+        np.testing.assert_array_equal(synth.block_order_permutation(T, Hs, Ws, P).numpy(),
+                                      oracle.token_order(T, Hs, Ws, P))

@@ -138,6 +138,50 @@ def cpu_baseline(w, x, thr: float, heads: int = 2) -> dict:
             "seconds": round(t_mask + t_fwd, 2)}
 
 
+def reorder_bench(w, dev, stream, iters: int) -> dict:
+    """Token reordering and its inverse on the workload's hidden states [B, S, H*D] bf16.
+
+    A pure permutation: the algorithmic traffic is one read and one write of the tensor."""
+    import torch
+    import block_sparse_attention_nabla_amd as nb
+    shape = (w.B, w.S, w.H * w.D)
+    g = torch.Generator(device=dev).manual_seed(7)
+    x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).bfloat16()
+    y = torch.empty_like(x)
+    z = torch.empty_like(x)
+    for _ in range(2):
+        nb.nabla_reorder_tokens(x, w.T, w.Hs, w.Ws, w.P, out=y, stream=stream)
+        nb.nabla_reorder_tokens(y, w.T, w.Hs, w.Ws, w.P, inverse=True, out=z, stream=stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(iters):
+        nb.nabla_reorder_tokens(x, w.T, w.Hs, w.Ws, w.P, out=y, stream=stream)
+    ev[1].record(stream)
+    for _ in range(iters):
+        nb.nabla_reorder_tokens(y, w.T, w.Hs, w.Ws, w.P, inverse=True, out=z, stream=stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    if not torch.equal(z.view(torch.int16), x.view(torch.int16)):
+        raise RuntimeError("token reordering round trip is not the identity")
+    nbytes = 2 * x.numel() * x.element_size()
+    fwd_ms = ev[0].elapsed_time(ev[1]) / iters
+    inv_ms = ev[1].elapsed_time(ev[2]) / iters
+    fwd_gbps = nbytes / (fwd_ms * 1e-3) / 1e9
+    inv_gbps = nbytes / (inv_ms * 1e-3) / 1e9
+    log(f"token reordering {shape} bf16: forward {fwd_ms * 1e3:.1f} us ({fwd_gbps:.0f} GB/s), "
+        f"inverse {inv_ms * 1e3:.1f} us ({inv_gbps:.0f} GB/s)")
+    return {
+        "kernel": "reorder_kernel",
+        "shape": list(shape), "dtype": "bf16", "patch": w.P,
+        "algorithmic_bytes_per_launch": nbytes,
+        "fwd_ms": round(fwd_ms, 4), "inv_ms": round(inv_ms, 4),
+        "fwd_gbps": round(fwd_gbps, 1), "inv_gbps": round(inv_gbps, 1),
+        "bound": "hbm", "peak_gbps": PEAK_HBM_GBPS,
+        "frac": round(max(fwd_gbps, inv_gbps) / PEAK_HBM_GBPS, 4),
+    }
+
+
 def train_step(args, dev, stream) -> dict:
     """Mask + forward + backward on the 2B-DiT training shape (B=2, H=16, S=61440,
     D=128; ~85% block sparsity). Every step rebuilds the mask from fresh Q/K
@@ -224,6 +268,9 @@ def main() -> int:
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training-step figures (2B-DiT shape, forward + backward)")
     ap.add_argument("--train-steps", type=int, default=4)
+    ap.add_argument("--no-reorder", action="store_true",
+                    help="skip the token reordering measurement")
+    ap.add_argument("--reorder-iters", type=int, default=10)
     args = ap.parse_args()
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic)))
@@ -376,6 +423,8 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if not args.no_reorder:
+        result["reorder"] = reorder_bench(w, dev, stream, args.reorder_iters)
     if not args.no_train:
         del o, lse, lists, ws_mask, ws_fwd, q, k, v
         torch.cuda.empty_cache()

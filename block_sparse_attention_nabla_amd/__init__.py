@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     nabla_sparse_attn_fwd(q, k, v, kv_count, kv_idx) -> (o, lse)
     nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx)
                                                      -> (dq, dk, dv)
+    nabla_reorder_tokens(x, T, Hs, Ws, P, inverse=False) -> reordered copy
     nabla_workspace_size(op, B, H, S, D, N), nabla_status_string(code)
 """
 
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "nabla_build_mask",
     "nabla_sparse_attn_fwd",
     "nabla_sparse_attn_bwd",
+    "nabla_reorder_tokens",
 )
 
 
@@ -79,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                           _vp, ctypes.c_size_t, _vp]
+    lib.nabla_reorder_tokens.restype = ctypes.c_int
+    lib.nabla_reorder_tokens.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int64,
+                                         _i32, _vp]
     _lib = lib
     return lib
 
@@ -237,8 +242,33 @@ def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx
     return dq, dk, dv
 
 
+def nabla_reorder_tokens(x: torch.Tensor, T: int, Hs: int, Ws: int, P: int, inverse: bool = False,
+                         *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Token reordering of section 3.1.1 (Figure 3) or its inverse, out of place.
+
+    ``x`` is a contiguous CUDA tensor [..., T*Hs*Ws, F] (any dtype): the
+    leading dimensions are items, each token's F features one row. Returns the
+    tokens in block order (``inverse=False``) or back in raster order."""
+    if not x.is_cuda or not x.is_contiguous() or x.dim() < 2:
+        raise ValueError("x must be a contiguous CUDA tensor [..., T*Hs*Ws, F]")
+    S = T * Hs * Ws
+    if x.shape[-2] != S:
+        raise ValueError(f"x has {x.shape[-2]} tokens, expected T*Hs*Ws = {S}")
+    items = x.numel() // max(S * x.shape[-1], 1) if x.numel() else 0
+    row_bytes = x.shape[-1] * x.element_size()
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of x's shape and dtype")
+    st = load_library().nabla_reorder_tokens(_ptr(x), _ptr(out), items, T, Hs, Ws, P, row_bytes,
+                                             1 if inverse else 0, _stream(x, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, "nabla_reorder_tokens")
+    return out
+
+
 __all__ = [
     "LIB_PATH", "BLOCK_N", "EXPORTED_SYMBOLS", "NablaError", "StaWindow", "load_library",
     "nabla_status_string", "nabla_workspace_size", "nabla_build_mask", "nabla_sparse_attn_fwd",
-    "nabla_sparse_attn_bwd", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD",
+    "nabla_sparse_attn_bwd", "nabla_reorder_tokens", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD",
 ]

@@ -27,6 +27,7 @@ SOURCES = [
     "schedule.hip",
     "attn_fwd.hip",
     "attn_bwd.hip",
+    "reorder.hip",
 ]
 
 HIPCC_FLAGS = [

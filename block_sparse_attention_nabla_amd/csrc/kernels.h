@@ -76,4 +76,8 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const XcdSchedule& sched, float softmax_scale, void* dq,
                          hipStream_t stream);
 
+// Token reordering (block order <-> raster order) of runs of P tokens; see reorder.hip.
+hipError_t launch_reorder(const void* src, void* dst, uint32_t runs, uint32_t cpr, uint32_t P,
+                          uint32_t tW, bool inverse, hipStream_t stream);
+
 }  // namespace nabla

@@ -150,4 +150,14 @@ nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v
     return NABLA_OK;
 }
 
+nabla_status_t nabla_reorder_tokens(const void* src, void* dst, int32_t B, int32_t T, int32_t Hs,
+                                    int32_t Ws, int32_t P, int64_t row_bytes, int32_t inverse,
+                                    void* stream) {
+    ReorderGeom g;
+    const nabla_status_t st = check_reorder(src, dst, B, T, Hs, Ws, P, row_bytes, inverse, &g);
+    if (st != NABLA_OK || g.empty) return st;
+    NABLA_LAUNCH(launch_reorder(src, dst, g.runs, g.cpr, g.P, g.tW, inverse != 0, as_stream(stream)));
+    return NABLA_OK;
+}
+
 }  // extern "C"

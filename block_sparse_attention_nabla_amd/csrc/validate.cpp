@@ -62,6 +62,37 @@ BwdWorkspace bwd_workspace(const Shape& s) {
     return w;
 }
 
+nabla_status_t check_reorder(const void* src, void* dst, int32_t B, int32_t T, int32_t Hs,
+                             int32_t Ws, int32_t P, int64_t row_bytes, int32_t inverse,
+                             ReorderGeom* out) {
+    if (B < 0 || T < 0 || Hs < 0 || Ws < 0 || P <= 0 || row_bytes <= 0) return NABLA_ERR_INVALID_ARG;
+    if (row_bytes % 16 != 0) return NABLA_ERR_INVALID_ARG;
+    if (Hs % P != 0 || Ws % P != 0) return NABLA_ERR_INVALID_ARG;
+    if (inverse != 0 && inverse != 1) return NABLA_ERR_INVALID_ARG;
+    const int64_t tokens = (int64_t)B * T * Hs * Ws;
+    ReorderGeom g{0, 0, (uint32_t)P, 0, tokens == 0};
+    if (g.empty) {
+        if (out) *out = g;
+        return NABLA_OK;
+    }
+    if (!src || !dst || !aligned16(src) || !aligned16(dst)) return NABLA_ERR_INVALID_ARG;
+    // Index arithmetic of the kernel is 32-bit in runs and in chunks per run.
+    if (row_bytes > ((int64_t)1 << 36)) return NABLA_ERR_UNSUPPORTED;
+    const int64_t runs = tokens / P;
+    const int64_t cpr = (int64_t)P * (row_bytes / 16);
+    if (runs > 0x7fffffff || cpr > 0x7fffffff) return NABLA_ERR_UNSUPPORTED;
+    // At most 2^40 chunks (16 TiB): far beyond any device, and no overflow below.
+    if ((uint64_t)runs * (uint64_t)cpr > ((uint64_t)1 << 40)) return NABLA_ERR_UNSUPPORTED;
+    const uint64_t bytes = (uint64_t)runs * (uint64_t)cpr * 16u;
+    const uintptr_t s = (uintptr_t)src, d = (uintptr_t)dst;
+    if (s < d + bytes && d < s + bytes) return NABLA_ERR_INVALID_ARG;  // overlap
+    g.runs = (uint32_t)runs;
+    g.cpr = (uint32_t)cpr;
+    g.tW = (uint32_t)(Ws / P);
+    if (out) *out = g;
+    return NABLA_OK;
+}
+
 uint64_t threshold_fixed(float thr) {
     const double x = (double)thr * 1099511627776.0;  // 2^40
     return (uint64_t)floor(x);

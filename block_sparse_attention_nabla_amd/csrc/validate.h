@@ -33,6 +33,16 @@ MaskWorkspace mask_workspace(const Shape& s);
 FwdWorkspace fwd_workspace(const Shape& s);
 BwdWorkspace bwd_workspace(const Shape& s);
 
+// Token reordering geometry: `runs` moved units of P tokens, `cpr` 16-byte
+// chunks per run, tW patches per frame row. empty = nothing to move.
+struct ReorderGeom {
+    uint32_t runs, cpr, P, tW;
+    bool empty;
+};
+nabla_status_t check_reorder(const void* src, void* dst, int32_t B, int32_t T, int32_t Hs,
+                             int32_t Ws, int32_t P, int64_t row_bytes, int32_t inverse,
+                             ReorderGeom* out);
+
 // Fixed-point threshold used by the selection kernel: floor(thr * 2^40).
 uint64_t threshold_fixed(float thr);
 

@@ -136,6 +136,31 @@ NABLA_API nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, con
                                      void* dk, void* dv, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/*
+ * Token reordering, section 3.1.1 (Figure 3): "fractal flattening", applied to
+ * the token sequence at the input of the network, and its inverse at the output.
+ * Each of the B items holds T frames of Hs x Ws tokens; raster order is
+ * (t, y, x) with x fastest. Block order groups the P x P tokens of each spatial
+ * patch into P*P consecutive tokens, row-major inside the patch, patches
+ * row-major inside the frame, frames in their original order: block-order
+ * position ((t*(Hs/P) + y/P)*(Ws/P) + x/P)*P*P + (y%P)*P + x%P holds raster
+ * token (t, y, x). With P*P == N the result is the block layout the other entry
+ * points expect.
+ * A token is an opaque row of row_bytes bytes, for example the C features of a
+ * hidden state ([B, S, C] with row_bytes = C * element size) or one head's D
+ * features ([B*H, S, D], passing B*H as B).
+ *   inverse = 0: src in raster order -> dst in block order;
+ *   inverse = 1: src in block order  -> dst in raster order.
+ * src, dst: device pointers, 16-byte aligned, B*T*Hs*Ws*row_bytes bytes each,
+ * not overlapping (out of place). row_bytes > 0 and a multiple of 16; P >= 1;
+ * Hs and Ws multiples of P (NABLA_ERR_INVALID_ARG otherwise). B, T, Hs or Ws
+ * equal to 0 is an empty permutation: NABLA_OK, nothing enqueued. A pure byte
+ * permutation: dst is bit-exact. No workspace.
+ */
+NABLA_API nabla_status_t nabla_reorder_tokens(const void* src, void* dst, int32_t B, int32_t T,
+                                              int32_t Hs, int32_t Ws, int32_t P, int64_t row_bytes,
+                                              int32_t inverse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

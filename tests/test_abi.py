@@ -146,3 +146,26 @@ def test_binding_requires_the_library(tmp_path):
             mod.load_library(str(tmp_path / "nope.so"))
     finally:
         mod._lib = saved
+
+
+def test_reorder_validation(lib):
+    f = lib.nabla_reorder_tokens
+
+    def call(src=P, dst=P2, B=1, T=2, Hs=16, Ws=16, Pt=8, row=256, inv=0):
+        return f(src, dst, B, T, Hs, Ws, Pt, row, inv, None)
+
+    assert call(Hs=12) == INVALID                      # Hs not a multiple of P
+    assert call(Ws=20) == INVALID
+    assert call(row=24) == INVALID                     # row not a multiple of 16
+    assert call(row=0) == INVALID
+    assert call(Pt=0) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(inv=2) == INVALID
+    assert call(src=None) == INVALID
+    assert call(dst=ctypes.c_void_p(0x7F0000100008)) == INVALID  # misaligned
+    assert call(dst=ctypes.c_void_p(0x7F0000000000 + 4096)) == INVALID  # overlaps src
+    assert call(B=1 << 20, T=1 << 10, Hs=64, Ws=64, Pt=1, row=16) == UNSUPPORTED
+    # Empty permutations enqueue nothing and need no pointers.
+    assert call(src=None, dst=None, B=0) == OK
+    assert call(src=None, dst=None, T=0) == OK
+    assert call(src=None, dst=None, Hs=0) == OK

@@ -30,6 +30,7 @@ _lib = None
 _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _i64 = ctypes.c_int64
 _dbl = ctypes.c_double
 _vp = ctypes.c_void_p
@@ -56,6 +57,7 @@ def _load():
     lib.nabla_oracle_reduced_map.argtypes = [_f64p, _f64p, _i64, _i64, _i64, _dbl, _f64p]
     lib.nabla_oracle_mass_above.argtypes = [_f64p, _i64, _i64, _f64p]
     lib.nabla_oracle_cdf_mask.argtypes = [_f64p, _i64, _dbl, _u8p]
+    lib.nabla_oracle_count_above.argtypes = [_f64p, _i64, _i64, _i64p]
     lib.nabla_oracle_sta_mask.argtypes = [_i64] * 7 + [_u8p]
     lib.nabla_oracle_union.argtypes = [_u8p, _u8p, _i64, _i64]
     lib.nabla_oracle_attn_fwd.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _u8p,
@@ -124,6 +126,32 @@ def cdf_mask(g: np.ndarray, thr: float) -> np.ndarray:
     return m
 
 
+def count_above(a: np.ndarray) -> np.ndarray:
+    """C_ij = number of entries of row i strictly larger than entry j -> [BH, n, n] int64."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    BH, n, _ = a.shape
+    c = np.empty(a.shape, dtype=np.int64)
+    _load().nabla_oracle_count_above(a, BH, n, c)
+    return c
+
+
+def topk_mask(a: np.ndarray, k: int) -> np.ndarray:
+    """Top-k selector: keep j iff fewer than k entries of its row are strictly larger (uint8).
+
+    Keeps the k largest entries of every row; entries tied at the k-th value are
+    kept together. k must be >= 1."""
+    if int(k) < 1:
+        raise ValueError("k must be >= 1")
+    return (count_above(a) < int(k)).astype(np.uint8)
+
+
+def sta_only_mask(BH: int, T: int, Hs: int, Ws: int, P: int, win_t: int, win_h: int,
+                  win_w: int) -> np.ndarray:
+    """The static STA selector on its own: the STA map for every head -> [BH, n, n] uint8."""
+    m = sta_mask(T, Hs, Ws, P, win_t, win_h, win_w)
+    return np.ascontiguousarray(np.broadcast_to(m, (BH,) + m.shape))
+
+
 def sta_mask(T: int, Hs: int, Ws: int, P: int, win_t: int, win_h: int, win_w: int) -> np.ndarray:
     """STA block map [n, n]: clipped window centred on the query tile (section 2.2, eq. (4))."""
     n = T * (Hs // P) * (Ws // P)
@@ -157,6 +185,22 @@ def build_mask(q, k, N: int, thr: float, sta: Optional[Dict[str, int]] = None,
                      sta["win_w"])
         m = union(m, s)
     return {"mask": m, "mask_nabla": nab, "a": a, "g": g, "qa": qa, "ka": ka}
+
+
+def build_topk_mask(q, k, N: int, topk: int, sta: Optional[Dict[str, int]] = None,
+                    scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Mask stage with the Top-k selector in place of the CDF rule: pool, reduced
+    softmax, keep the top-k blocks of every row, optional STA union."""
+    qa, ka = pool(q, N), pool(k, N)
+    D = qa.shape[-1]
+    a = reduced_map(qa, ka, (1.0 / math.sqrt(D)) if scale is None else scale)
+    m = topk_mask(a, topk)
+    sel = m
+    if sta is not None:
+        s = sta_mask(sta["T"], sta["Hs"], sta["Ws"], sta["P"], sta["win_t"], sta["win_h"],
+                     sta["win_w"])
+        m = union(m, s)
+    return {"mask": m, "mask_topk": sel, "a": a, "qa": qa, "ka": ka}
 
 
 def mask_to_lists(mask: np.ndarray) -> Dict[str, np.ndarray]:

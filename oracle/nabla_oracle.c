@@ -116,6 +116,26 @@ EXPORT void nabla_oracle_mass_above(const double* a, int64_t BH, int64_t n, doub
     }
 }
 
+/* Top-k selector, the fixed-budget alternative the CDF rule is compared with
+ * (review record of arXiv 2507.13546, comment on Appendix C, Theorem 1): for
+ * every entry j of a row, c[j] = number of entries of the same row strictly
+ * larger than a[j]. Keeping j iff c[j] < k keeps the k largest entries, with
+ * entries tied at the k-th value kept together (the same tie rule as G). */
+EXPORT void nabla_oracle_count_above(const double* a, int64_t BH, int64_t n, int64_t* c) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        for (int64_t i = 0; i < n; ++i) {
+            const double* row = a + (bh * n + i) * n;
+            int64_t* crow = c + (bh * n + i) * n;
+            for (int64_t j = 0; j < n; ++j) {
+                int64_t cnt = 0;
+                for (int64_t l = 0; l < n; ++l) cnt += row[l] > row[j];
+                crow[j] = cnt;
+            }
+        }
+    }
+}
+
 /* Binarisation (Algorithm 1, step 10 in the G form): keep iff thr >= 1 or
  * G <= thr. count = number of entries of g and m. */
 EXPORT void nabla_oracle_cdf_mask(const double* g, int64_t count, double thr, uint8_t* m) {

@@ -138,6 +138,51 @@ def cpu_baseline(w, x, thr: float, heads: int = 2) -> dict:
             "seconds": round(t_mask + t_fwd, 2)}
 
 
+def selector_bench(w, q, k, v, lists, ws_mask, ws_fwd, o, lse, stream, iters: int,
+                   topk: int, sta_win) -> dict:
+    """The variant selectors on the same layer: Top-k blocks (k = topk) and the
+    static STA window alone, each followed by the same forward kernel."""
+    import torch
+    import block_sparse_attention_nabla_amd as nb
+    B, H, S, D, n = w.B, w.H, w.S, w.D, w.n
+    sta = dict(T=w.T, Hs=w.Hs, Ws=w.Ws, P=w.P, win_t=sta_win[0], win_h=sta_win[1], win_w=sta_win[2])
+    ws_sta = torch.empty(nb.nabla_workspace_size(nb.NABLA_OP_STA_MASK, B, H, S, D), dtype=torch.uint8,
+                         device=q.device)
+    makers = {
+        "topk": lambda: nb.nabla_build_topk_mask(q, k, topk, out=lists, workspace=ws_mask, stream=stream),
+        "sta_only": lambda: nb.nabla_build_sta_mask(B, H, S, sta, q.device, out=lists, workspace=ws_sta,
+                                                    stream=stream),
+    }
+    res = {}
+    for name, make in makers.items():
+        def fwd():
+            nb.nabla_sparse_attn_fwd(q, k, v, lists["kv_count"], lists["kv_idx"], o=o, lse=lse,
+                                     workspace=ws_fwd, stream=stream)
+        make()
+        fwd()
+        torch.cuda.synchronize()
+        kept = int(lists["kv_count"].sum())
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
+        for i in range(iters):
+            ev[i][0].record(stream)
+            make()
+            ev[i][1].record(stream)
+            fwd()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        mask_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / iters
+        fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / iters
+        flops = kept * 4.0 * w.N * w.N * D
+        res[name] = {
+            "selector": f"top-{topk} blocks per row" if name == "topk" else f"STA{tuple(sta_win)} window alone",
+            "block_sparsity": round(1.0 - kept / (B * H * n * n), 5),
+            "mask_ms": round(mask_ms, 4), "forward_ms": round(fwd_ms, 4),
+            "forward_tflops": round(flops / (fwd_ms * 1e-3) / 1e12, 2),
+        }
+        log(f"selector {name}: {res[name]}")
+    return res
+
+
 def reorder_bench(w, dev, stream, iters: int) -> dict:
     """Token reordering and its inverse on the workload's hidden states [B, S, H*D] bf16.
 
@@ -268,6 +313,8 @@ def main() -> int:
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training-step figures (2B-DiT shape, forward + backward)")
     ap.add_argument("--train-steps", type=int, default=4)
+    ap.add_argument("--no-selectors", action="store_true",
+                    help="skip the Top-k and STA-only selector measurement")
     ap.add_argument("--no-reorder", action="store_true",
                     help="skip the token reordering measurement")
     ap.add_argument("--reorder-iters", type=int, default=10)
@@ -423,6 +470,11 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if not args.no_selectors:
+        # Top-k at the CDF rule's mean kept count; STA at Table 1's (18, 24, 24) window.
+        topk = max(1, round(kept / (B * H * n)))
+        result["selectors"] = selector_bench(w, q, k, v, lists, ws_mask, ws_fwd, o, lse, stream, 5,
+                                             topk, (18, 24, 24))
     if not args.no_reorder:
         result["reorder"] = reorder_bench(w, dev, stream, args.reorder_iters)
     if not args.no_train:

@@ -7,6 +7,8 @@ library is not built, every call raises.
 
 Entry points (same names as the C ABI):
     nabla_build_mask(q, k, thr, sta=None, ...)      -> dict of block lists
+    nabla_build_topk_mask(q, k, topk, sta=None, ...) -> dict of block lists (Top-k selector)
+    nabla_build_sta_mask(B, H, S, sta, device, ...)  -> dict of block lists (STA alone)
     nabla_sparse_attn_fwd(q, k, v, kv_count, kv_idx) -> (o, lse)
     nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx)
                                                      -> (dq, dk, dv)
@@ -27,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnabla.so")
 
 NABLA_OK = 0
-NABLA_OP_MASK, NABLA_OP_FWD, NABLA_OP_BWD = 0, 1, 2
+NABLA_OP_MASK, NABLA_OP_FWD, NABLA_OP_BWD, NABLA_OP_STA_MASK = 0, 1, 2, 3
 NABLA_DTYPE_BF16, NABLA_DTYPE_FP32 = 0, 1
 BLOCK_N = 64
 
@@ -35,6 +37,8 @@ EXPORTED_SYMBOLS = (
     "nabla_workspace_size",
     "nabla_status_string",
     "nabla_build_mask",
+    "nabla_build_topk_mask",
+    "nabla_build_sta_mask",
     "nabla_sparse_attn_fwd",
     "nabla_sparse_attn_bwd",
     "nabla_reorder_tokens",
@@ -74,6 +78,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_build_mask.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                      ctypes.POINTER(StaWindow), _vp, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_size_t, _vp]
+    lib.nabla_build_topk_mask.restype = ctypes.c_int
+    lib.nabla_build_topk_mask.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          ctypes.POINTER(StaWindow), _vp, _vp, _vp, _vp, _vp, _vp,
+                                          ctypes.c_size_t, _vp]
+    lib.nabla_build_sta_mask.restype = ctypes.c_int
+    lib.nabla_build_sta_mask.argtypes = [_i32, _i32, _i32, _i32, ctypes.POINTER(StaWindow), _vp, _vp,
+                                         _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.nabla_sparse_attn_fwd.restype = ctypes.c_int
     lib.nabla_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                           ctypes.c_float, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp]
@@ -120,6 +131,45 @@ def _workspace(op, B, H, S, D, N, device, workspace):
     return workspace, size
 
 
+def _mask_outputs(B, H, n, dev, transpose, dense, out):
+    out = dict(out or {})
+    res = {}
+    keys = [("kv_count", (B, H, n), torch.int32), ("kv_idx", (B, H, n, n), torch.int32)]
+    if transpose:
+        keys += [("q_count", (B, H, n), torch.int32), ("q_idx", (B, H, n, n), torch.int32)]
+    if dense:
+        keys += [("dense_mask", (B, H, n, n), torch.uint8)]
+    for key, shape, dtype in keys:
+        t = out.get(key)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+        if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"out[{key!r}] must be a contiguous {dtype} tensor of shape {shape}")
+        res[key] = t
+    return res
+
+
+def _sta_ptr(sta: Optional[dict]):
+    if sta is None:
+        return None
+    return ctypes.pointer(StaWindow(*(int(sta[f]) for f in ("T", "Hs", "Ws", "P", "win_t", "win_h", "win_w"))))
+
+
+def _content_mask(fn_name, q, k, select_arg, sta, N, transpose, dense, out, workspace, stream):
+    _check_qkv("q", q)
+    B, H, S, D = q.shape
+    _check_qkv("k", k, q.shape)
+    res = _mask_outputs(B, H, S // N, q.device, transpose, dense, out)
+    ws, size = _workspace(NABLA_OP_MASK, B, H, S, D, N, q.device, workspace)
+    st = getattr(load_library(), fn_name)(
+        _ptr(q), _ptr(k), B, H, S, D, N, select_arg, _sta_ptr(sta), _ptr(res["kv_count"]),
+        _ptr(res["kv_idx"]), _ptr(res.get("q_count")), _ptr(res.get("q_idx")),
+        _ptr(res.get("dense_mask")), _ptr(ws), ws.numel(), _stream(q, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, fn_name)
+    return res
+
+
 def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, sta: Optional[dict] = None,
                      N: int = BLOCK_N, *, transpose: bool = False, dense: bool = False,
                      out: Optional[Dict[str, torch.Tensor]] = None,
@@ -130,39 +180,42 @@ def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, sta: Optional
     (``transpose``) and dense_mask uint8 [B,H,n,n] (``dense``). ``sta`` holds
     T, Hs, Ws, P, win_t, win_h, win_w.
     """
-    _check_qkv("q", q)
-    B, H, S, D = q.shape
-    _check_qkv("k", k, q.shape)
-    n = S // N
-    dev = q.device
-    out = dict(out or {})
-    kv_count = out.get("kv_count")
-    if kv_count is None:
-        kv_count = torch.empty((B, H, n), dtype=torch.int32, device=dev)
-    kv_idx = out.get("kv_idx")
-    if kv_idx is None:
-        kv_idx = torch.empty((B, H, n, n), dtype=torch.int32, device=dev)
-    res = {"kv_count": kv_count, "kv_idx": kv_idx}
-    q_count = q_idx = dmask = None
-    if transpose:
-        q_count = out.get("q_count")
-        q_count = torch.empty((B, H, n), dtype=torch.int32, device=dev) if q_count is None else q_count
-        q_idx = out.get("q_idx")
-        q_idx = torch.empty((B, H, n, n), dtype=torch.int32, device=dev) if q_idx is None else q_idx
-        res.update(q_count=q_count, q_idx=q_idx)
-    if dense:
-        dmask = out.get("dense_mask")
-        dmask = torch.empty((B, H, n, n), dtype=torch.uint8, device=dev) if dmask is None else dmask
-        res["dense_mask"] = dmask
-    ws, size = _workspace(NABLA_OP_MASK, B, H, S, D, N, dev, workspace)
-    sta_ptr = None
-    if sta is not None:
-        sta_ptr = ctypes.pointer(StaWindow(*(int(sta[f]) for f in ("T", "Hs", "Ws", "P", "win_t", "win_h", "win_w"))))
-    st = load_library().nabla_build_mask(
-        _ptr(q), _ptr(k), B, H, S, D, N, float(thr), sta_ptr, _ptr(kv_count), _ptr(kv_idx),
-        _ptr(q_count), _ptr(q_idx), _ptr(dmask), _ptr(ws), ws.numel(), _stream(q, stream))
+    return _content_mask("nabla_build_mask", q, k, float(thr), sta, N, transpose, dense, out,
+                         workspace, stream)
+
+
+def nabla_build_topk_mask(q: torch.Tensor, k: torch.Tensor, topk: int, sta: Optional[dict] = None,
+                          N: int = BLOCK_N, *, transpose: bool = False, dense: bool = False,
+                          out: Optional[Dict[str, torch.Tensor]] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> Dict[str, torch.Tensor]:
+    """Top-k selector: the topk largest reduced-map blocks of every row (ties kept
+    together) [+ STA union]. Same outputs as nabla_build_mask."""
+    return _content_mask("nabla_build_topk_mask", q, k, int(topk), sta, N, transpose, dense, out,
+                         workspace, stream)
+
+
+def nabla_build_sta_mask(B: int, H: int, S: int, sta: dict, device, N: int = BLOCK_N, *,
+                         transpose: bool = False, dense: bool = False,
+                         out: Optional[Dict[str, torch.Tensor]] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> Dict[str, torch.Tensor]:
+    """The static STA window alone (section 2.2), as lists for every head."""
+    device = torch.device(device)
+    if device.type != "cuda":
+        raise ValueError("device must be a CUDA device")
+    if sta is None:
+        raise ValueError("the STA-only selector needs the sta window")
+    res = _mask_outputs(B, H, S // N, device, transpose, dense, out)
+    ws, size = _workspace(NABLA_OP_STA_MASK, B, H, S, 0, N, device, workspace)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    st = load_library().nabla_build_sta_mask(
+        B, H, S, N, _sta_ptr(sta), _ptr(res["kv_count"]), _ptr(res["kv_idx"]),
+        _ptr(res.get("q_count")), _ptr(res.get("q_idx")), _ptr(res.get("dense_mask")), _ptr(ws),
+        ws.numel(), ctypes.c_void_p(stream.cuda_stream))
     if st != NABLA_OK:
-        raise NablaError(st, "nabla_build_mask")
+        raise NablaError(st, "nabla_build_sta_mask")
     return res
 
 
@@ -269,6 +322,7 @@ def nabla_reorder_tokens(x: torch.Tensor, T: int, Hs: int, Ws: int, P: int, inve
 
 __all__ = [
     "LIB_PATH", "BLOCK_N", "EXPORTED_SYMBOLS", "NablaError", "StaWindow", "load_library",
-    "nabla_status_string", "nabla_workspace_size", "nabla_build_mask", "nabla_sparse_attn_fwd",
-    "nabla_sparse_attn_bwd", "nabla_reorder_tokens", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD",
+    "nabla_status_string", "nabla_workspace_size", "nabla_build_mask", "nabla_build_topk_mask",
+    "nabla_build_sta_mask", "nabla_sparse_attn_fwd",
+    "nabla_sparse_attn_bwd", "nabla_reorder_tokens", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD", "NABLA_OP_STA_MASK",
 ]

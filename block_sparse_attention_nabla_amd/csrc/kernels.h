@@ -20,8 +20,11 @@ hipError_t launch_pool(const void* q, const void* k, float* qa, float* ka, int64
                        hipStream_t stream);
 hipError_t launch_logits(const float* qa, const float* ka, float* logits, int64_t BH, int n, int D,
                          float scale, hipStream_t stream);
-hipError_t launch_select(const float* logits, int64_t BH, int n, int keep_all, uint64_t thr_fixed,
-                         const StaParams& sta, int32_t* kv_count, int32_t* kv_idx,
+// Row selectors of launch_select. bound: kSelCdf -> floor(thr * 2^40) (fixed-point
+// mass); kSelTopk -> k - 1 (a count); kSelSta -> unused (logits may be null).
+enum { kSelCdf = 0, kSelTopk = 1, kSelSta = 2 };
+hipError_t launch_select(int mode, const float* logits, int64_t BH, int n, int keep_all,
+                         uint64_t bound, const StaParams& sta, int32_t* kv_count, int32_t* kv_idx,
                          uint8_t* dense_mask, uint32_t* bits, int words_per_row,
                          hipStream_t stream);
 hipError_t launch_transpose(const uint32_t* bits, int64_t BH, int n, int words_per_row,

@@ -9,7 +9,10 @@
 //   logits_kernel    steps 6-7 (logits part): Q_a K_a^T * scale per head, fp32 MFMA
 //   select_kernel    steps 7-11: row softmax, sort-free CDF selection by radix
 //                    select over the fp32 bit patterns of the probabilities,
-//                    STA union, ascending compaction, optional dense/bit rows
+//                    STA union, ascending compaction, optional dense/bit rows.
+//                    The same kernel also runs the two variant selectors the
+//                    CDF rule is measured against: Top-k blocks per row, and
+//                    the static STA window alone (Table 1's baseline).
 //   transpose_kernel the key-block -> query-block lists the backward pass uses
 
 #include "common.h"
@@ -136,6 +139,13 @@ __device__ __forceinline__ bool sta_contains(const StaParams& s, int i, int j) {
 // ---------------------------------------------------------------------------
 // Selection + compaction: one workgroup (256 threads) per query block row.
 //
+// kSelCdf:  keep j iff G_j <= thr (the NABLA rule, Algorithm 1).
+// kSelTopk: keep j iff fewer than k entries of the row are strictly larger than
+//           p_j (the k largest, ties at the k-th value kept together). The
+//           radix select below runs unchanged with every entry weighing 1
+//           instead of its fixed-point mass, and with k - 1 as the bound.
+// kSelSta:  keep j iff the STA window of i contains j; no softmax, no selection.
+//
 // p_j = exp(L_j - max) / sum is computed in fp32. The kept set is
 // {j : G_j <= thr} with G_j = mass of entries strictly larger than p_j; it is
 // exactly {j : p_j >= tau} for the smallest probability value tau whose
@@ -148,8 +158,9 @@ __device__ __forceinline__ bool sta_contains(const StaParams& s, int i, int j) {
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 256;
 
+template <int MODE>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const float* __restrict__ logits, int n, int keep_all, uint64_t thr_fixed, StaParams sta,
+    const float* __restrict__ logits, int n, int keep_all, uint64_t bound, StaParams sta,
     int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_idx,
     uint8_t* __restrict__ dense_mask, uint32_t* __restrict__ bits, int words_per_row) {
     __shared__ float pv[NABLA_MAX_BLOCKS];
@@ -164,82 +175,86 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int64_t row = blockIdx.x;  // flattened bh * n + i
     const int i = (int)(row % n);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const float* L = logits + row * (int64_t)n;
-
-    // 1. load the row, row maximum
-    float mx = -INFINITY;
-    for (int j = t; j < n; j += kSelThreads) {
-        const float x = L[j];
-        pv[j] = x;
-        mx = fmaxf(mx, x);
-    }
-    mx = wave_max(mx);
-    if (lane == 0) wred[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-    __syncthreads();
-
-    // 2. exponentials and their sum (fixed order per thread, then fixed tree)
-    float z = 0.f;
-    for (int j = t; j < n; j += kSelThreads) {
-        const float e = expf(pv[j] - mx);
-        pv[j] = e;
-        z += e;
-    }
-    z = wave_sum(z);
-    if (lane == 0) wred[wave] = z;
-    __syncthreads();
-    z = (wred[0] + wred[1]) + (wred[2] + wred[3]);
-    for (int j = t; j < n; j += kSelThreads) pv[j] = pv[j] / z;
-    __syncthreads();
-
-    // 3. radix select of tau over the bit patterns of p
-    uint32_t prefix = 0, pmask = 0;
-    unsigned long long above = 0;  // fixed-point mass strictly above the current prefix range
-    if (!keep_all) {
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            hmass[t] = 0ull;
-            hcnt[t] = 0;
-            __syncthreads();
-            for (int j = t; j < n; j += kSelThreads) {
-                const float p = pv[j];
-                const uint32_t key = __float_as_uint(p);
-                if ((key & pmask) == prefix) {
-                    const int d = (key >> shift) & 255;
-                    atomicAdd(&hmass[d], (unsigned long long)__float2ull_rn(p * 0x1p40f));
-                    atomicAdd(&hcnt[d], 1);
-                }
-            }
-            __syncthreads();
-            // Suffix sum over bins: bin t needs the mass of bins > t. Each
-            // thread owns bin t; inclusive suffix scan within the wave over
-            // lanes (higher lane = higher bin), then add the higher waves.
-            unsigned long long m = hmass[t];
-            unsigned long long incl = m;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const unsigned long long o = __shfl_down(incl, off);
-                if (lane + off < 64) incl += o;
-            }
-            if (lane == 0) wsum[wave] = incl;  // total of this wave's 64 bins
-            if (t == 0) sel_bin = 256;
-            __syncthreads();
-            unsigned long long higher = 0;
-            for (int w = wave + 1; w < 4; ++w) higher += wsum[w];
-            const unsigned long long mass_above_bin = above + higher + (incl - m);
-            if (hcnt[t] > 0 && mass_above_bin <= thr_fixed) atomicMin(&sel_bin, t);
-            __syncthreads();
-            const int b = sel_bin;  // always < 256: the highest non-empty bin qualifies
-            if (t == b) sel_above = mass_above_bin;
-            __syncthreads();
-            above = sel_above;
-            prefix |= (uint32_t)b << shift;
-            pmask |= 0xffu << shift;
-            __syncthreads();
+    uint32_t tau = 0;
+    if (MODE != kSelSta) {
+        const float* L = logits + row * (int64_t)n;
+        // 1. load the row, row maximum
+        float mx = -INFINITY;
+        for (int j = t; j < n; j += kSelThreads) {
+            const float x = L[j];
+            pv[j] = x;
+            mx = fmaxf(mx, x);
         }
-    }
-    const uint32_t tau = prefix;
+        mx = wave_max(mx);
+        if (lane == 0) wred[wave] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+        __syncthreads();
+
+        // 2. exponentials and their sum (fixed order per thread, then fixed tree)
+        float z = 0.f;
+        for (int j = t; j < n; j += kSelThreads) {
+            const float e = expf(pv[j] - mx);
+            pv[j] = e;
+            z += e;
+        }
+        z = wave_sum(z);
+        if (lane == 0) wred[wave] = z;
+        __syncthreads();
+        z = (wred[0] + wred[1]) + (wred[2] + wred[3]);
+        for (int j = t; j < n; j += kSelThreads) pv[j] = pv[j] / z;
+        __syncthreads();
+
+        // 3. radix select of tau over the bit patterns of p
+        uint32_t prefix = 0, pmask = 0;
+        unsigned long long above = 0;  // weight (mass or count) strictly above the prefix range
+        if (!keep_all) {
+            for (int pass = 0; pass < 4; ++pass) {
+                const int shift = 24 - 8 * pass;
+                hmass[t] = 0ull;
+                hcnt[t] = 0;
+                __syncthreads();
+                for (int j = t; j < n; j += kSelThreads) {
+                    const float p = pv[j];
+                    const uint32_t key = __float_as_uint(p);
+                    if ((key & pmask) == prefix) {
+                        const int d = (key >> shift) & 255;
+                        const unsigned long long wgt =
+                            MODE == kSelTopk ? 1ull : (unsigned long long)__float2ull_rn(p * 0x1p40f);
+                        atomicAdd(&hmass[d], wgt);
+                        atomicAdd(&hcnt[d], 1);
+                    }
+                }
+                __syncthreads();
+                // Suffix sum over bins: bin t needs the mass of bins > t. Each
+                // thread owns bin t; inclusive suffix scan within the wave over
+                // lanes (higher lane = higher bin), then add the higher waves.
+                unsigned long long m = hmass[t];
+                unsigned long long incl = m;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const unsigned long long o = __shfl_down(incl, off);
+                    if (lane + off < 64) incl += o;
+                }
+                if (lane == 0) wsum[wave] = incl;  // total of this wave's 64 bins
+                if (t == 0) sel_bin = 256;
+                __syncthreads();
+                unsigned long long higher = 0;
+                for (int w = wave + 1; w < 4; ++w) higher += wsum[w];
+                const unsigned long long mass_above_bin = above + higher + (incl - m);
+                if (hcnt[t] > 0 && mass_above_bin <= bound) atomicMin(&sel_bin, t);
+                __syncthreads();
+                const int b = sel_bin;  // always < 256: the highest non-empty bin qualifies
+                if (t == b) sel_above = mass_above_bin;
+                __syncthreads();
+                above = sel_above;
+                prefix |= (uint32_t)b << shift;
+                pmask |= 0xffu << shift;
+                __syncthreads();
+            }
+        }
+        tau = prefix;
+    }  // MODE != kSelSta
 
     // 4. decisions, STA union, ascending compaction
     int32_t* out_idx = kv_idx + row * (int64_t)n;
@@ -248,7 +263,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const int j = base + t;
         bool keep = false;
         if (j < n) {
-            keep = keep_all || __float_as_uint(pv[j]) >= tau;
+            if (MODE != kSelSta) keep = keep_all || __float_as_uint(pv[j]) >= tau;
             if (!keep && sta.on) keep = sta_contains(sta, i, j);
         }
         const unsigned long long bal = __ballot(keep);
@@ -332,12 +347,20 @@ hipError_t launch_logits(const float* qa, const float* ka, float* logits, int64_
     return hipGetLastError();
 }
 
-hipError_t launch_select(const float* logits, int64_t BH, int n, int keep_all, uint64_t thr_fixed,
-                         const StaParams& sta, int32_t* kv_count, int32_t* kv_idx,
+hipError_t launch_select(int mode, const float* logits, int64_t BH, int n, int keep_all,
+                         uint64_t bound, const StaParams& sta, int32_t* kv_count, int32_t* kv_idx,
                          uint8_t* dense_mask, uint32_t* bits, int words_per_row,
                          hipStream_t stream) {
-    select_kernel<<<(unsigned)(BH * n), kSelThreads, 0, stream>>>(
-        logits, n, keep_all, thr_fixed, sta, kv_count, kv_idx, dense_mask, bits, words_per_row);
+    const unsigned grid = (unsigned)(BH * n);
+    if (mode == kSelTopk)
+        select_kernel<kSelTopk><<<grid, kSelThreads, 0, stream>>>(
+            logits, n, keep_all, bound, sta, kv_count, kv_idx, dense_mask, bits, words_per_row);
+    else if (mode == kSelSta)
+        select_kernel<kSelSta><<<grid, kSelThreads, 0, stream>>>(
+            logits, n, keep_all, bound, sta, kv_count, kv_idx, dense_mask, bits, words_per_row);
+    else
+        select_kernel<kSelCdf><<<grid, kSelThreads, 0, stream>>>(
+            logits, n, keep_all, bound, sta, kv_count, kv_idx, dense_mask, bits, words_per_row);
     return hipGetLastError();
 }
 

@@ -20,6 +20,55 @@ inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; 
         if ((expr) != hipSuccess) return NABLA_ERR_HIP; \
     } while (0)
 
+StaParams sta_params(const nabla_sta_t* sta) {
+    StaParams sp{};
+    if (sta) {
+        sp.on = 1;
+        sp.tT = sta->T;
+        sp.tH = sta->Hs / sta->P;
+        sp.tW = sta->Ws / sta->P;
+        sp.wt = sta->win_t;
+        sp.wh = sta->win_h / sta->P;
+        sp.ww = sta->win_w / sta->P;
+    }
+    return sp;
+}
+
+// Pool, reduced logits, one selector (kSelCdf or kSelTopk), compaction and the
+// optional transpose. Arguments other than the selector's are validated here.
+nabla_status_t content_mask(int mode, int keep_all, uint64_t bound, const void* q, const void* k,
+                            int32_t B, int32_t H, int32_t S, int32_t D, int32_t N,
+                            const nabla_sta_t* sta, int32_t* kv_count, int32_t* kv_idx,
+                            int32_t* q_count, int32_t* q_idx, uint8_t* dense_mask, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    Shape s;
+    nabla_status_t st = check_shape(B, H, S, D, N, &s);
+    if (st != NABLA_OK) return st;
+    if (!q || !k || !kv_count || !kv_idx) return NABLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k)) return NABLA_ERR_INVALID_ARG;
+    if ((q_count == nullptr) != (q_idx == nullptr)) return NABLA_ERR_INVALID_ARG;
+    st = check_sta(sta, s);
+    if (st != NABLA_OK) return st;
+    const MaskWorkspace w = mask_workspace(s);
+    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
+
+    const StaParams sp = sta_params(sta);
+    float* qa = reinterpret_cast<float*>(ws_at(workspace, w.qa));
+    float* ka = reinterpret_cast<float*>(ws_at(workspace, w.ka));
+    float* logits = reinterpret_cast<float*>(ws_at(workspace, w.logits));
+    uint32_t* bits = q_idx ? reinterpret_cast<uint32_t*>(ws_at(workspace, w.bits)) : nullptr;
+    hipStream_t hs = as_stream(stream);
+
+    NABLA_LAUNCH(launch_pool(q, k, qa, ka, s.BH * s.n, (int)s.D, hs));
+    NABLA_LAUNCH(launch_logits(qa, ka, logits, s.BH, (int)s.n, (int)s.D,
+                               1.0f / sqrtf((float)s.D), hs));
+    NABLA_LAUNCH(launch_select(mode, logits, s.BH, (int)s.n, keep_all, bound, sp, kv_count, kv_idx,
+                               dense_mask, bits, w.words_per_row, hs));
+    if (q_idx)
+        NABLA_LAUNCH(launch_transpose(bits, s.BH, (int)s.n, w.words_per_row, q_count, q_idx, hs));
+    return NABLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -37,8 +86,10 @@ const char* nabla_status_string(nabla_status_t status) {
 
 size_t nabla_workspace_size(int32_t op, int32_t B, int32_t H, int32_t S, int32_t D, int32_t N) {
     Shape s;
+    if (op == NABLA_OP_STA_MASK) D = kStaShapeD;  // the STA mask does not depend on D
     if (check_shape(B, H, S, D, N, &s) != NABLA_OK) return 0;
     switch (op) {
+        case NABLA_OP_STA_MASK: return sta_workspace(s).total;
         case NABLA_OP_MASK: return mask_workspace(s).total;
         case NABLA_OP_FWD: return fwd_workspace(s).total;
         case NABLA_OP_BWD: return bwd_workspace(s).total;
@@ -51,39 +102,41 @@ nabla_status_t nabla_build_mask(const void* q, const void* k, int32_t B, int32_t
                                 int32_t* kv_count, int32_t* kv_idx, int32_t* q_count,
                                 int32_t* q_idx, uint8_t* dense_mask, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-    Shape s;
-    nabla_status_t st = check_shape(B, H, S, D, N, &s);
-    if (st != NABLA_OK) return st;
-    if (!q || !k || !kv_count || !kv_idx) return NABLA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k)) return NABLA_ERR_INVALID_ARG;
-    if ((q_count == nullptr) != (q_idx == nullptr)) return NABLA_ERR_INVALID_ARG;
     if (!(thr >= 0.0f) || isinf(thr)) return NABLA_ERR_INVALID_ARG;  // rejects NaN too
+    return content_mask(kSelCdf, thr >= 1.0f, threshold_fixed(thr), q, k, B, H, S, D, N, sta,
+                        kv_count, kv_idx, q_count, q_idx, dense_mask, workspace, workspace_bytes,
+                        stream);
+}
+
+nabla_status_t nabla_build_topk_mask(const void* q, const void* k, int32_t B, int32_t H, int32_t S,
+                                     int32_t D, int32_t N, int32_t topk, const nabla_sta_t* sta,
+                                     int32_t* kv_count, int32_t* kv_idx, int32_t* q_count,
+                                     int32_t* q_idx, uint8_t* dense_mask, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    if (topk < 1) return NABLA_ERR_INVALID_ARG;
+    const int keep_all = N > 0 && S / N <= topk;
+    return content_mask(kSelTopk, keep_all, (uint64_t)(topk - 1), q, k, B, H, S, D, N, sta,
+                        kv_count, kv_idx, q_count, q_idx, dense_mask, workspace, workspace_bytes,
+                        stream);
+}
+
+nabla_status_t nabla_build_sta_mask(int32_t B, int32_t H, int32_t S, int32_t N,
+                                    const nabla_sta_t* sta, int32_t* kv_count, int32_t* kv_idx,
+                                    int32_t* q_count, int32_t* q_idx, uint8_t* dense_mask,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    Shape s;
+    nabla_status_t st = check_shape(B, H, S, kStaShapeD, N, &s);
+    if (st != NABLA_OK) return st;
+    if (!sta || !kv_count || !kv_idx) return NABLA_ERR_INVALID_ARG;
+    if ((q_count == nullptr) != (q_idx == nullptr)) return NABLA_ERR_INVALID_ARG;
     st = check_sta(sta, s);
     if (st != NABLA_OK) return st;
-    const MaskWorkspace w = mask_workspace(s);
+    const StaWorkspace w = sta_workspace(s);
     if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
 
-    StaParams sp{};
-    if (sta) {
-        sp.on = 1;
-        sp.tT = sta->T;
-        sp.tH = sta->Hs / sta->P;
-        sp.tW = sta->Ws / sta->P;
-        sp.wt = sta->win_t;
-        sp.wh = sta->win_h / sta->P;
-        sp.ww = sta->win_w / sta->P;
-    }
-    float* qa = reinterpret_cast<float*>(ws_at(workspace, w.qa));
-    float* ka = reinterpret_cast<float*>(ws_at(workspace, w.ka));
-    float* logits = reinterpret_cast<float*>(ws_at(workspace, w.logits));
     uint32_t* bits = q_idx ? reinterpret_cast<uint32_t*>(ws_at(workspace, w.bits)) : nullptr;
     hipStream_t hs = as_stream(stream);
-    const int keep_all = thr >= 1.0f;
-
-    NABLA_LAUNCH(launch_pool(q, k, qa, ka, s.BH * s.n, (int)s.D, hs));
-    NABLA_LAUNCH(launch_logits(qa, ka, logits, s.BH, (int)s.n, (int)s.D,
-                               1.0f / sqrtf((float)s.D), hs));
-    NABLA_LAUNCH(launch_select(logits, s.BH, (int)s.n, keep_all, threshold_fixed(thr), sp, kv_count,
+    NABLA_LAUNCH(launch_select(kSelSta, nullptr, s.BH, (int)s.n, 0, 0, sta_params(sta), kv_count,
                                kv_idx, dense_mask, bits, w.words_per_row, hs));
     if (q_idx)
         NABLA_LAUNCH(launch_transpose(bits, s.BH, (int)s.n, w.words_per_row, q_count, q_idx, hs));

@@ -46,6 +46,14 @@ MaskWorkspace mask_workspace(const Shape& s) {
     return w;
 }
 
+StaWorkspace sta_workspace(const Shape& s) {
+    StaWorkspace w;
+    w.words_per_row = (int)((s.n + 31) / 32);
+    w.bits = 0;
+    w.total = align256((size_t)s.BH * s.n * w.words_per_row * sizeof(uint32_t));
+    return w;
+}
+
 FwdWorkspace fwd_workspace(const Shape& s) {
     FwdWorkspace w;
     w.order = 0;

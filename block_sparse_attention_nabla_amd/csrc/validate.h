@@ -18,6 +18,10 @@ struct MaskWorkspace {
     size_t qa, ka, logits, bits, total;
     int words_per_row;
 };
+struct StaWorkspace {
+    size_t bits, total;
+    int words_per_row;
+};
 struct FwdWorkspace {
     size_t order, total;
 };
@@ -30,7 +34,11 @@ nabla_status_t check_sta(const nabla_sta_t* sta, const Shape& s);
 bool aligned16(const void* p);
 
 MaskWorkspace mask_workspace(const Shape& s);
+StaWorkspace sta_workspace(const Shape& s);
 FwdWorkspace fwd_workspace(const Shape& s);
+
+// The STA-only mask has no head dimension; its shape checks use this one.
+constexpr int32_t kStaShapeD = 64;
 BwdWorkspace bwd_workspace(const Shape& s);
 
 // Token reordering geometry: `runs` moved units of P tokens, `cpr` 16-byte

@@ -66,7 +66,9 @@ typedef struct {
     int32_t win_t, win_h, win_w;
 } nabla_sta_t;
 
-enum { NABLA_OP_MASK = 0, NABLA_OP_FWD = 1, NABLA_OP_BWD = 2 };
+/* Operations for nabla_workspace_size. NABLA_OP_MASK covers nabla_build_mask and
+ * nabla_build_topk_mask; NABLA_OP_STA_MASK covers nabla_build_sta_mask (D ignored). */
+enum { NABLA_OP_MASK = 0, NABLA_OP_FWD = 1, NABLA_OP_BWD = 2, NABLA_OP_STA_MASK = 3 };
 
 /* Element type of the forward output O. */
 enum { NABLA_DTYPE_BF16 = 0, NABLA_DTYPE_FP32 = 1 };
@@ -96,6 +98,39 @@ NABLA_API nabla_status_t nabla_build_mask(const void* q, const void* k, int32_t 
                                 int32_t* kv_count, int32_t* kv_idx, int32_t* q_count,
                                 int32_t* q_idx, uint8_t* dense_mask, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Variant selector: Top-k blocks per row, the fixed-budget rule the CDF
+ * selection is compared with (review record of arXiv 2507.13546 on
+ * pith.science, referee comment on Appendix C, Theorem 1). Same pooling and
+ * reduced softmax as nabla_build_mask; then, for every head and query block i,
+ *   keep j iff fewer than topk entries p_il are strictly larger than p_ij
+ * (the topk largest blocks; blocks tied at the topk-th value are all kept, so
+ * a row keeps at least min(topk, n) blocks), then the STA union if sta != NULL.
+ * topk >= 1 (NABLA_ERR_INVALID_ARG otherwise); topk >= n keeps every block.
+ * Outputs, workspace (NABLA_OP_MASK) and errors as for nabla_build_mask.
+ */
+NABLA_API nabla_status_t nabla_build_topk_mask(const void* q, const void* k, int32_t B, int32_t H,
+                                               int32_t S, int32_t D, int32_t N, int32_t topk,
+                                               const nabla_sta_t* sta, int32_t* kv_count,
+                                               int32_t* kv_idx, int32_t* q_count, int32_t* q_idx,
+                                               uint8_t* dense_mask, void* workspace,
+                                               size_t workspace_bytes, void* stream);
+
+/*
+ * Variant selector: the static sliding-tile mask alone (STA, section 2.2,
+ * eq. (4)-(5); the STA rows of Table 1): keep j iff the clipped window centred
+ * on query tile i contains tile j, for every one of the B*H heads. Needs no Q
+ * or K. sta is required (same rules as in nabla_build_mask, with P*P == N and
+ * T*Hs*Ws == S). Outputs as for nabla_build_mask; the workspace
+ * (NABLA_OP_STA_MASK, only used when q_count/q_idx are requested, but always
+ * checked) holds the row bitmasks of the transpose.
+ */
+NABLA_API nabla_status_t nabla_build_sta_mask(int32_t B, int32_t H, int32_t S, int32_t N,
+                                              const nabla_sta_t* sta, int32_t* kv_count,
+                                              int32_t* kv_idx, int32_t* q_count, int32_t* q_idx,
+                                              uint8_t* dense_mask, void* workspace,
+                                              size_t workspace_bytes, void* stream);
 
 /*
  * Block-sparse attention forward (eq. (4) with the kept-block mask): for each

@@ -10,6 +10,11 @@ Mask: the GPU's block mask must equal the oracle's exactly, except
       unexplained mismatch and fails.
 STA-covered blocks are decided by integer logic and are never excused.
 
+Top-k: the same, with the selector's own rule: a mismatch is excused only when
+the number of entries that could lie strictly above p_ij under the REL_TIE
+perturbation straddles k (p_ij ties with the k-th largest value within fp32
+rounding). STA-covered blocks are never excused.
+
 Attention: outputs are compared element by element with the oracle run on the
 GPU's own mask, so mask and attention checks stay independent.
 """
@@ -58,6 +63,27 @@ def compare_masks(gpu_mask: np.ndarray, orc: Dict[str, np.ndarray], thr: float,
     res["tie_excused"] = tie
     res["unexplained"] = int((mism & ~(in_band & excusable)).sum()) - tie
     return res
+
+
+def compare_topk_masks(gpu_mask: np.ndarray, orc: Dict[str, np.ndarray], k: int,
+                       sta: Optional[np.ndarray] = None) -> Dict[str, int]:
+    gpu = np.asarray(gpu_mask).astype(bool)
+    exp = np.asarray(orc["mask"]).astype(bool)
+    assert gpu.shape == exp.shape, (gpu.shape, exp.shape)
+    p = orc["a"]
+    mism = gpu != exp
+    excusable = np.ones_like(mism) if sta is None else ~np.broadcast_to(sta.astype(bool), mism.shape)
+    tie = 0
+    for idx in zip(*np.nonzero(mism & excusable)):
+        row = p[idx[:-1]]
+        pj = row[idx[-1]]
+        others = np.delete(row, idx[-1])
+        c_lo = int((others > pj * (1 + REL_TIE)).sum())    # surely above
+        c_hi = int((others >= pj * (1 - REL_TIE)).sum())   # possibly above
+        if c_lo < k <= c_hi:
+            tie += 1
+    return {"blocks": int(exp.size), "kept_oracle": int(exp.sum()), "kept_gpu": int(gpu.sum()),
+            "mismatch": int(mism.sum()), "tie_excused": tie, "unexplained": int(mism.sum()) - tie}
 
 
 def lists_to_mask(kv_count: np.ndarray, kv_idx: np.ndarray) -> np.ndarray:

@@ -169,3 +169,40 @@ def test_reorder_validation(lib):
     assert call(src=None, dst=None, B=0) == OK
     assert call(src=None, dst=None, T=0) == OK
     assert call(src=None, dst=None, Hs=0) == OK
+
+
+def test_topk_validation(lib):
+    f = lib.nabla_build_topk_mask
+
+    def call(S=1024, D=64, topk=4, q=P, sta=None, ws=P2, wsb=BIG):
+        return f(q, P, 1, 2, S, D, 64, topk, sta, P, P, None, None, None, ws, wsb, None)
+
+    assert call(topk=0) == INVALID
+    assert call(topk=-3) == INVALID
+    assert call(S=1000) == INVALID
+    assert call(D=96) == UNSUPPORTED
+    assert call(q=None) == INVALID
+    assert call(wsb=16) == WORKSPACE
+
+
+def test_sta_mask_validation(lib):
+    f = lib.nabla_build_sta_mask
+    good = dict(T=4, Hs=16, Ws=16, P=8, win_t=3, win_h=8, win_w=8)
+
+    def sta(**over):
+        d = dict(good, **over)
+        return ctypes.pointer(nb.StaWindow(*(d[k] for k in ("T", "Hs", "Ws", "P", "win_t", "win_h", "win_w"))))
+
+    def call(S=1024, s=None, cnt=P, ws=P2, wsb=BIG, qc=None, qi=None):
+        return f(1, 2, S, 64, s, cnt, P, qc, qi, None, ws, wsb, None)
+
+    assert call(s=None) == INVALID                       # the window is required
+    assert call(s=sta(T=5)) == INVALID                   # T*Hs*Ws != S
+    assert call(s=sta(win_h=12)) == INVALID
+    assert call(s=sta(), cnt=None) == INVALID
+    assert call(s=sta(), qc=P) == INVALID                # q_count without q_idx
+    assert call(s=sta(), ws=None) == WORKSPACE
+    assert call(s=sta(), wsb=16) == WORKSPACE
+    # The STA workspace ignores D and holds one bitmask row per query block.
+    size = nb.nabla_workspace_size(nb.NABLA_OP_STA_MASK, 1, 2, 1024, 0)
+    assert size >= 2 * 16 * 4 and size == nb.nabla_workspace_size(nb.NABLA_OP_STA_MASK, 1, 2, 1024, 128)

@@ -58,6 +58,8 @@ def _load():
     lib.nabla_oracle_mass_above.argtypes = [_f64p, _i64, _i64, _f64p]
     lib.nabla_oracle_cdf_mask.argtypes = [_f64p, _i64, _dbl, _u8p]
     lib.nabla_oracle_count_above.argtypes = [_f64p, _i64, _i64, _i64p]
+    lib.nabla_oracle_block_mass.argtypes = [_f32p, _f32p, _i64, _i64, _i64, _i64, _dbl, _vp, _i64,
+                                            _f64p]
     lib.nabla_oracle_sta_mask.argtypes = [_i64] * 7 + [_u8p]
     lib.nabla_oracle_union.argtypes = [_u8p, _u8p, _i64, _i64]
     lib.nabla_oracle_attn_fwd.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _u8p,
@@ -309,3 +311,40 @@ def blocks_to_tokens(x: np.ndarray, T: int, Hs: int, Ws: int, P: int) -> np.ndar
     out = np.empty_like(x)
     out[..., token_order(T, Hs, Ws, P), :] = x
     return out
+
+
+# ----------------------------------------------------------------------------
+# Mask-fidelity diagnostic: the per-block fidelity test the review record of
+# arXiv 2507.13546 (pith.science) asks for -- how much of full attention's
+# token-level probability mass falls inside the kept blocks, against the best
+# blocks one could keep with the same per-row budget.
+# ----------------------------------------------------------------------------
+def block_mass(q, k, N: int, scale: Optional[float] = None,
+               blocks: Optional[Sequence[int]] = None) -> np.ndarray:
+    """M_ij = mean over the N queries of block i of the dense softmax mass on key block j.
+
+    Returns [BH, n, n] fp64; rows not listed in ``blocks`` are NaN."""
+    q, k = _as_f32(q), _as_f32(k)
+    BH, S, D = q.shape
+    n = S // N
+    sc = (1.0 / math.sqrt(D)) if scale is None else float(scale)
+    m = np.full((BH, n, n), np.nan, dtype=np.float64)
+    arr, cnt = _blocks_arg(blocks)
+    _load().nabla_oracle_block_mass(q, k, BH, S, D, N, sc,
+                                    arr.ctypes.data if arr is not None else None, cnt, m)
+    return m
+
+
+def mask_recall(mass: np.ndarray, mask: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per row: (mass inside the kept blocks, mass inside the c best blocks), c = kept count.
+
+    The second is the top-mass block oracle at the same per-row budget: the sum of
+    the row's c largest block masses (a sort; ties do not change the sum)."""
+    mass = np.asarray(mass, dtype=np.float64)
+    keep = np.asarray(mask).astype(bool)
+    recall = np.where(keep, mass, 0.0).sum(axis=-1)
+    c = keep.sum(axis=-1)
+    desc = -np.sort(-mass, axis=-1)
+    csum = np.concatenate([np.zeros(mass.shape[:-1] + (1,)), np.cumsum(desc, axis=-1)], axis=-1)
+    best = np.take_along_axis(csum, c[..., None], axis=-1)[..., 0]
+    return recall, best

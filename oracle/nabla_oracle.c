@@ -177,6 +177,56 @@ EXPORT void nabla_oracle_union(uint8_t* m, const uint8_t* sta, int64_t BH, int64
     for (int64_t e = 0; e < BH * n * n; ++e) m[e] = (uint8_t)(m[e] | sta[e % (n * n)]);
 }
 
+/* Mask-fidelity diagnostic (review record of arXiv 2507.13546 on pith.science:
+ * the referee's per-block fidelity test and the skeptic's falsifier). True block
+ * mass of full (dense) attention: for query block i and key block j,
+ *   M_ij = (1/N) * sum over tokens s of block i, u of block j of P_su,
+ *   P_su = exp(x_su - m_s) / sum_{u'} exp(x_su' - m_s),  x_su = scale * q_s . k_u,
+ * the softmax running over ALL S keys (eq. (2)). Each row of M sums to 1.
+ * blocks lists flattened query blocks (bh*n + i) to compute (NULL = all);
+ * m is [BH][n][n] and only the listed rows are written. */
+EXPORT void nabla_oracle_block_mass(const float* q, const float* k, int64_t BH, int64_t S,
+                                    int64_t D, int64_t N, double scale, const int64_t* blocks,
+                                    int64_t nblocks, double* m) {
+    const int64_t n = S / N;
+    const int64_t total = blocks ? nblocks : BH * n;
+#pragma omp parallel
+    {
+        double* x = (double*)malloc(sizeof(double) * S);
+        double* row = (double*)malloc(sizeof(double) * n);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < total; ++t) {
+            const int64_t blk = blocks ? blocks[t] : t;
+            const int64_t bh = blk / n, i = blk % n;
+            for (int64_t j = 0; j < n; ++j) row[j] = 0.0;
+            for (int64_t r = 0; r < N; ++r) {
+                const float* qs = q + (bh * S + i * N + r) * D;
+                double mx = -INFINITY;
+                for (int64_t u = 0; u < S; ++u) {
+                    const float* ku = k + (bh * S + u) * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += (double)qs[d] * (double)ku[d];
+                    x[u] = scale * dot;
+                    if (x[u] > mx) mx = x[u];
+                }
+                double z = 0.0;
+                for (int64_t u = 0; u < S; ++u) {
+                    x[u] = exp(x[u] - mx);
+                    z += x[u];
+                }
+                for (int64_t j = 0; j < n; ++j) {
+                    double sj = 0.0;
+                    for (int64_t c = 0; c < N; ++c) sj += x[j * N + c];
+                    row[j] += sj / z;
+                }
+            }
+            for (int64_t j = 0; j < n; ++j) m[(bh * n + i) * n + j] = row[j] / (double)N;
+        }
+        free(x);
+        free(row);
+    }
+}
+
 /* Kept keys of query block i: the tokens of every block j with mask[i][j]. */
 static int64_t kept_keys(const uint8_t* mrow, int64_t n, int64_t N, int64_t* keys) {
     int64_t c = 0;

@@ -138,10 +138,27 @@ def cpu_baseline(w, x, thr: float, heads: int = 2) -> dict:
             "seconds": round(t_mask + t_fwd, 2)}
 
 
+def recall_summary(nb, mass, lists) -> dict:
+    """Mask fidelity of block lists: mass of dense attention inside the kept blocks,
+    against the best blocks at the same per-row count (per-row means and tails)."""
+    import torch
+    rec, best = nb.nabla_mask_recall(mass, lists["kv_count"], lists["kv_idx"])
+    r = rec.reshape(-1).double()
+    b = best.reshape(-1).double()
+    return {
+        "mean_recall": round(float(r.mean()), 5),
+        "mean_best_recall": round(float(b.mean()), 5),
+        "recall_p01": round(float(torch.quantile(r.float().cpu(), 0.01)), 5),
+        "min_recall": round(float(r.min()), 5),
+        "mean_gap_to_best": round(float((b - r).mean()), 5),
+    }
+
+
 def selector_bench(w, q, k, v, lists, ws_mask, ws_fwd, o, lse, stream, iters: int,
-                   topk: int, sta_win) -> dict:
+                   topk: int, sta_win, mass=None) -> dict:
     """The variant selectors on the same layer: Top-k blocks (k = topk) and the
-    static STA window alone, each followed by the same forward kernel."""
+    static STA window alone, each followed by the same forward kernel. With the
+    dense block mass, also the fidelity of each selector's lists."""
     import torch
     import block_sparse_attention_nabla_amd as nb
     B, H, S, D, n = w.B, w.H, w.S, w.D, w.n
@@ -179,6 +196,8 @@ def selector_bench(w, q, k, v, lists, ws_mask, ws_fwd, o, lse, stream, iters: in
             "mask_ms": round(mask_ms, 4), "forward_ms": round(fwd_ms, 4),
             "forward_tflops": round(flops / (fwd_ms * 1e-3) / 1e12, 2),
         }
+        if mass is not None:
+            res[name]["fidelity"] = recall_summary(nb, mass, lists)
         log(f"selector {name}: {res[name]}")
     return res
 
@@ -313,6 +332,8 @@ def main() -> int:
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training-step figures (2B-DiT shape, forward + backward)")
     ap.add_argument("--train-steps", type=int, default=4)
+    ap.add_argument("--no-fidelity", action="store_true",
+                    help="skip the mask-fidelity diagnostic (needs the dense run)")
     ap.add_argument("--no-selectors", action="store_true",
                     help="skip the Top-k and STA-only selector measurement")
     ap.add_argument("--no-reorder", action="store_true",
@@ -418,6 +439,29 @@ def main() -> int:
             f"speedup {speedup:.2f}x at density {1 - sparsity:.4f} (linearity {speedup * (1 - sparsity):.3f})")
         del dense_lists
 
+    # Mask fidelity: true block mass of dense attention (the dense run above left
+    # the dense LSE in `lse`), and the recall of the 90% CDF lists.
+    mass = None
+    fidelity = None
+    if args.dense_iters > 0 and not args.no_fidelity:
+        mass = torch.empty((B, H, n, n), dtype=torch.float32, device=dev)
+        nb.nabla_block_mass(q, k, lse, out=mass, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        nb.nabla_block_mass(q, k, lse, out=mass, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mass_ms = e0.elapsed_time(e1)
+        mass_flops = 2.0 * B * H * S * S * D
+        fidelity = {
+            "what": "dense attention mass inside the kept blocks vs the best blocks at the same per-row count",
+            "block_mass_kernel_ms": round(mass_ms, 3),
+            "block_mass_tflops": round(mass_flops / (mass_ms * 1e-3) / 1e12, 1),
+            "cdf": recall_summary(nb, mass, lists),
+        }
+        log(f"fidelity: {fidelity}")
+
     if args.traffic_calibration:
         xa = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
         ya = torch.empty_like(xa)
@@ -474,7 +518,10 @@ def main() -> int:
         # Top-k at the CDF rule's mean kept count; STA at Table 1's (18, 24, 24) window.
         topk = max(1, round(kept / (B * H * n)))
         result["selectors"] = selector_bench(w, q, k, v, lists, ws_mask, ws_fwd, o, lse, stream, 5,
-                                             topk, (18, 24, 24))
+                                             topk, (18, 24, 24), mass)
+    if fidelity is not None:
+        result["fidelity"] = fidelity
+        del mass
     if not args.no_reorder:
         result["reorder"] = reorder_bench(w, dev, stream, args.reorder_iters)
     if not args.no_train:

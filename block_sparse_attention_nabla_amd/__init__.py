@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
     nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx)
                                                      -> (dq, dk, dv)
     nabla_reorder_tokens(x, T, Hs, Ws, P, inverse=False) -> reordered copy
+    nabla_block_mass(q, k, lse)                      -> dense block masses [B,H,n,n]
+    nabla_mask_recall(mass, kv_count, kv_idx)        -> (recall, best_recall) per row
     nabla_workspace_size(op, B, H, S, D, N), nabla_status_string(code)
 """
 
@@ -42,6 +44,8 @@ EXPORTED_SYMBOLS = (
     "nabla_sparse_attn_fwd",
     "nabla_sparse_attn_bwd",
     "nabla_reorder_tokens",
+    "nabla_block_mass",
+    "nabla_mask_recall",
 )
 
 
@@ -92,6 +96,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                           _vp, ctypes.c_size_t, _vp]
+    lib.nabla_block_mass.restype = ctypes.c_int
+    lib.nabla_block_mass.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp,
+                                     _vp]
+    lib.nabla_mask_recall.restype = ctypes.c_int
+    lib.nabla_mask_recall.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.nabla_reorder_tokens.restype = ctypes.c_int
     lib.nabla_reorder_tokens.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int64,
                                          _i32, _vp]
@@ -295,6 +304,49 @@ def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx
     return dq, dk, dv
 
 
+def nabla_block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor,
+                     softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """True block mass of dense attention, M [B,H,n,n] fp32 (rows sum to 1).
+
+    ``lse`` is the dense log-sum-exp [B,H,S] fp32, e.g. from nabla_sparse_attn_fwd
+    over lists that keep every block."""
+    _check_qkv("q", q)
+    B, H, S, D = q.shape
+    _check_qkv("k", k, q.shape)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, S]")
+    n = S // N
+    if out is None:
+        out = torch.empty((B, H, n, n), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, n, n) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor [B, H, n, n]")
+    scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    st = load_library().nabla_block_mass(_ptr(q), _ptr(k), _ptr(lse), B, H, S, D, N, scale, _ptr(out),
+                                         _stream(q, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, "nabla_block_mass")
+    return out
+
+
+def nabla_mask_recall(mass: torch.Tensor, kv_count: torch.Tensor, kv_idx: torch.Tensor,
+                      N: int = BLOCK_N, *, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per row: block mass inside the kept lists, and inside the best blocks at the same count."""
+    if not mass.is_cuda or mass.dtype != torch.float32 or mass.dim() != 4 or not mass.is_contiguous():
+        raise ValueError("mass must be a contiguous float32 CUDA tensor [B, H, n, n]")
+    B, H, n, _ = mass.shape
+    for name, t, shp in (("kv_count", kv_count, (B, H, n)), ("kv_idx", kv_idx, (B, H, n, n))):
+        if t.dtype != torch.int32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor of shape {shp}")
+    recall = torch.empty((B, H, n), dtype=torch.float32, device=mass.device)
+    best = torch.empty_like(recall)
+    st = load_library().nabla_mask_recall(_ptr(mass), B, H, n * N, N, _ptr(kv_count), _ptr(kv_idx),
+                                          _ptr(recall), _ptr(best), _stream(mass, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, "nabla_mask_recall")
+    return recall, best
+
+
 def nabla_reorder_tokens(x: torch.Tensor, T: int, Hs: int, Ws: int, P: int, inverse: bool = False,
                          *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Token reordering of section 3.1.1 (Figure 3) or its inverse, out of place.
@@ -324,5 +376,5 @@ __all__ = [
     "LIB_PATH", "BLOCK_N", "EXPORTED_SYMBOLS", "NablaError", "StaWindow", "load_library",
     "nabla_status_string", "nabla_workspace_size", "nabla_build_mask", "nabla_build_topk_mask",
     "nabla_build_sta_mask", "nabla_sparse_attn_fwd",
-    "nabla_sparse_attn_bwd", "nabla_reorder_tokens", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD", "NABLA_OP_STA_MASK",
+    "nabla_sparse_attn_bwd", "nabla_reorder_tokens", "nabla_block_mass", "nabla_mask_recall", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD", "NABLA_OP_STA_MASK",
 ]

@@ -28,6 +28,7 @@ SOURCES = [
     "attn_fwd.hip",
     "attn_bwd.hip",
     "reorder.hip",
+    "fidelity.hip",
 ]
 
 HIPCC_FLAGS = [

@@ -48,16 +48,22 @@ struct XcdSchedule {
 };
 XcdSchedule make_schedule(int64_t BH, int n);
 
-// Work item of workgroup b, or -1 for a padding slot.
-__device__ __forceinline__ int64_t scheduled_item(const XcdSchedule& s, const int32_t* order,
-                                                  int64_t b) {
+// Slot (head * n + position) of workgroup b, or -1 for a padding slot.
+__device__ __forceinline__ int64_t scheduled_slot(const XcdSchedule& s, int64_t b) {
     const int64_t x = b % 8, m = b / 8;
     const int64_t unit = x + 8 * (m / s.cap);
     const int64_t head = unit / s.parts;
     const int part = (int)(unit % s.parts);
     const int64_t pos = part + (int64_t)s.parts * (m % s.cap);
     if (pos >= s.n) return -1;
-    return order[head * s.n + pos];
+    return head * s.n + pos;
+}
+
+// Work item of workgroup b (through a per-head order), or -1 for a padding slot.
+__device__ __forceinline__ int64_t scheduled_item(const XcdSchedule& s, const int32_t* order,
+                                                  int64_t b) {
+    const int64_t slot = scheduled_slot(s, b);
+    return slot < 0 ? -1 : order[slot];
 }
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t BH, int S, int D,
@@ -78,6 +84,14 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
                          const XcdSchedule& sched, float softmax_scale, void* dq,
                          hipStream_t stream);
+
+// Mask-fidelity diagnostic (fidelity.hip): dense block masses from Q, K and the
+// dense LSE; per-row recall of block lists and of the best blocks at equal count.
+hipError_t launch_block_mass(const void* q, const void* k, const float* lse, int64_t BH, int S,
+                             int D, float softmax_scale, float* mass, hipStream_t stream);
+hipError_t launch_mask_recall(const float* mass, int64_t BH, int n, const int32_t* kv_count,
+                              const int32_t* kv_idx, float* recall, float* best,
+                              hipStream_t stream);
 
 // Token reordering (block order <-> raster order) of runs of P tokens; see reorder.hip.
 hipError_t launch_reorder(const void* src, void* dst, uint32_t runs, uint32_t cpr, uint32_t P,

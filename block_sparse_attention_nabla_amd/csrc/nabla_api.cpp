@@ -203,6 +203,32 @@ nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v
     return NABLA_OK;
 }
 
+nabla_status_t nabla_block_mass(const void* q, const void* k, const float* lse, int32_t B, int32_t H,
+                                int32_t S, int32_t D, int32_t N, float softmax_scale, float* mass,
+                                void* stream) {
+    Shape s;
+    const nabla_status_t st = check_shape(B, H, S, D, N, &s);
+    if (st != NABLA_OK) return st;
+    if (!q || !k || !lse || !mass) return NABLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k)) return NABLA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || isinf(softmax_scale)) return NABLA_ERR_INVALID_ARG;
+    NABLA_LAUNCH(launch_block_mass(q, k, lse, s.BH, (int)s.S, (int)s.D, softmax_scale, mass,
+                                   as_stream(stream)));
+    return NABLA_OK;
+}
+
+nabla_status_t nabla_mask_recall(const float* mass, int32_t B, int32_t H, int32_t S, int32_t N,
+                                 const int32_t* kv_count, const int32_t* kv_idx, float* recall,
+                                 float* best_recall, void* stream) {
+    Shape s;
+    const nabla_status_t st = check_shape(B, H, S, kStaShapeD, N, &s);
+    if (st != NABLA_OK) return st;
+    if (!mass || !kv_count || !kv_idx || !recall || !best_recall) return NABLA_ERR_INVALID_ARG;
+    NABLA_LAUNCH(launch_mask_recall(mass, s.BH, (int)s.n, kv_count, kv_idx, recall, best_recall,
+                                    as_stream(stream)));
+    return NABLA_OK;
+}
+
 nabla_status_t nabla_reorder_tokens(const void* src, void* dst, int32_t B, int32_t T, int32_t Hs,
                                     int32_t Ws, int32_t P, int64_t row_bytes, int32_t inverse,
                                     void* stream) {

@@ -37,7 +37,8 @@ MaskWorkspace mask_workspace(const Shape& s);
 StaWorkspace sta_workspace(const Shape& s);
 FwdWorkspace fwd_workspace(const Shape& s);
 
-// The STA-only mask has no head dimension; its shape checks use this one.
+// Shape checks of calls that have no head dimension (the STA-only mask, the
+// recall of block lists) use this one.
 constexpr int32_t kStaShapeD = 64;
 BwdWorkspace bwd_workspace(const Shape& s);
 

@@ -172,6 +172,38 @@ NABLA_API nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, con
                                      void* stream);
 
 /*
+ * Mask-fidelity diagnostic, part 1: the true block mass of full attention, the
+ * quantity of the per-block fidelity test asked for in the review record of
+ * arXiv 2507.13546 (pith.science: the referee's first major comment and the
+ * skeptic's falsifier). For every head, query block i and key block j:
+ *   mass[b, h, i, j] = (1/N) sum_{s in block i} sum_{u in block j} exp(scale q_s . k_u - lse_s)
+ * with lse the dense (all-keys) log-sum-exp of eq. (2) -- for instance the lse
+ * that nabla_sparse_attn_fwd returns for lists that keep every block. Each row
+ * then sums to 1. q, k: bf16 [B, H, S, D] in block order; lse: fp32 [B, H, S]
+ * (natural log); mass: fp32 [B, H, n, n] output. softmax_scale > 0, finite. Costs
+ * one dense Q K^T (2 S^2 D flop per head) on bf16 MFMA with fp32 sums; no
+ * workspace; deterministic.
+ */
+NABLA_API nabla_status_t nabla_block_mass(const void* q, const void* k, const float* lse, int32_t B,
+                                          int32_t H, int32_t S, int32_t D, int32_t N,
+                                          float softmax_scale, float* mass, void* stream);
+
+/*
+ * Mask-fidelity diagnostic, part 2: for every row (b, h, i) of a block mass
+ * (from nabla_block_mass) and block lists (from any nabla_build_*_mask),
+ *   recall[b, h, i]      = sum of mass[b, h, i, j] over the kept j,
+ *   best_recall[b, h, i] = sum of the c largest mass[b, h, i, :], c = kv_count --
+ * the top-mass block oracle at the same per-row budget, so recall <= best_recall.
+ * mass: fp32 [B, H, n, n]; kv_count/kv_idx as everywhere (indices outside [0, n)
+ * are ignored, counts clamped to [0, n]); recall, best_recall: fp32 [B, H, n]
+ * outputs. Sums in double, deterministic; no workspace. S and N as for the
+ * other calls (S % N == 0, N == 64).
+ */
+NABLA_API nabla_status_t nabla_mask_recall(const float* mass, int32_t B, int32_t H, int32_t S,
+                                           int32_t N, const int32_t* kv_count, const int32_t* kv_idx,
+                                           float* recall, float* best_recall, void* stream);
+
+/*
  * Token reordering, section 3.1.1 (Figure 3): "fractal flattening", applied to
  * the token sequence at the input of the network, and its inverse at the output.
  * Each of the B items holds T frames of Hs x Ws tokens; raster order is

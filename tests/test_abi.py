@@ -206,3 +206,17 @@ def test_sta_mask_validation(lib):
     # The STA workspace ignores D and holds one bitmask row per query block.
     size = nb.nabla_workspace_size(nb.NABLA_OP_STA_MASK, 1, 2, 1024, 0)
     assert size >= 2 * 16 * 4 and size == nb.nabla_workspace_size(nb.NABLA_OP_STA_MASK, 1, 2, 1024, 128)
+
+
+def test_fidelity_validation(lib):
+    bm = lib.nabla_block_mass
+    assert bm(P, P, P, 1, 2, 1000, 64, 64, 0.125, P, None) == INVALID      # S % N
+    assert bm(P, P, None, 1, 2, 1024, 64, 64, 0.125, P, None) == INVALID   # lse required
+    assert bm(P, P, P, 1, 2, 1024, 64, 64, 0.125, None, None) == INVALID   # mass required
+    assert bm(P, P, P, 1, 2, 1024, 64, 64, 0.0, P, None) == INVALID
+    assert bm(P, P, P, 1, 2, 1024, 96, 64, 0.125, P, None) == UNSUPPORTED
+    rc = lib.nabla_mask_recall
+    assert rc(P, 1, 2, 1000, 64, P, P, P, P, None) == INVALID
+    assert rc(None, 1, 2, 1024, 64, P, P, P, P, None) == INVALID
+    assert rc(P, 1, 2, 1024, 64, P, P, P, None, None) == INVALID
+    assert rc(P, 1, 2, 1024, 32, P, P, P, P, None) == UNSUPPORTED

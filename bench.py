@@ -43,7 +43,9 @@ if ROOT not in sys.path:
 METRIC = "effective TFLOP/s on kept blocks (% bf16 MFMA peak) + speedup vs dense at ~90% sparsity"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-FWD_KERNEL = "attn_fwd_kernel"
+# The forward kernel that bench.py times: the paired kernel when the frame hint is
+# given (the default), the one-block kernel with --no-pairs.
+FWD_KERNEL = "attn_fwd_pair_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan14b_720p_traffic.json")
 FWD_SOURCE = os.path.join(ROOT, "block_sparse_attention_nabla_amd", "csrc", "attn_fwd.hip")
 
@@ -155,7 +157,7 @@ def recall_summary(nb, mass, lists) -> dict:
 
 
 def selector_bench(w, q, k, v, lists, ws_mask, ws_fwd, o, lse, stream, iters: int,
-                   topk: int, sta_win, mass=None) -> dict:
+                   topk: int, sta_win, mass=None, frame_blocks: int = 0) -> dict:
     """The variant selectors on the same layer: Top-k blocks (k = topk) and the
     static STA window alone, each followed by the same forward kernel. With the
     dense block mass, also the fidelity of each selector's lists."""
@@ -174,7 +176,7 @@ def selector_bench(w, q, k, v, lists, ws_mask, ws_fwd, o, lse, stream, iters: in
     for name, make in makers.items():
         def fwd():
             nb.nabla_sparse_attn_fwd(q, k, v, lists["kv_count"], lists["kv_idx"], o=o, lse=lse,
-                                     workspace=ws_fwd, stream=stream)
+                                     workspace=ws_fwd, stream=stream, frame_blocks=frame_blocks)
         make()
         fwd()
         torch.cuda.synchronize()
@@ -256,6 +258,7 @@ def train_step(args, dev, stream) -> dict:
 
     w = synth.get_workload("dit2b_train")
     thr = w.thr_for(0.85)
+    fb = 0 if args.no_pairs else (w.Hs // w.P) * (w.Ws // w.P)
     B, H, S, D, n = w.B, w.H, w.S, w.D, w.n
     steps = max(1, args.train_steps)
     t0 = time.time()
@@ -278,7 +281,8 @@ def train_step(args, dev, stream) -> dict:
                             workspace=ws[nb.NABLA_OP_MASK], stream=stream)
         if ev: ev[1].record(stream)
         nb.nabla_sparse_attn_fwd(x["q"], x["k"], x["v"], lists["kv_count"], lists["kv_idx"], o=o,
-                                 lse=lse, workspace=ws[nb.NABLA_OP_FWD], stream=stream)
+                                 lse=lse, workspace=ws[nb.NABLA_OP_FWD], stream=stream,
+                                 frame_blocks=fb)
         if ev: ev[2].record(stream)
         nb.nabla_sparse_attn_bwd(x["q"], x["k"], x["v"], o, d_o, lse, lists["kv_count"],
                                  lists["kv_idx"], lists["q_count"], lists["q_idx"], dq=dq, dk=dk,
@@ -311,6 +315,7 @@ def train_step(args, dev, stream) -> dict:
         "backward_tflops": round(2.5 * kept_last * fpk / (bwd_ms * 1e-3) / 1e12, 1),
         "step_tflops": round(3.5 * kept_last * fpk / (wall * 1e-3) / 1e12, 1),
         "flop_model": "forward 4*N*N*D, backward 10*N*N*D per kept block pair",
+        "frame_blocks": fb,
     }
     log(f"train: {res}")
     return res
@@ -332,6 +337,8 @@ def main() -> int:
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training-step figures (2B-DiT shape, forward + backward)")
     ap.add_argument("--train-steps", type=int, default=4)
+    ap.add_argument("--no-pairs", action="store_true",
+                    help="no frame hint: one query block per forward workgroup")
     ap.add_argument("--no-fidelity", action="store_true",
                     help="skip the mask-fidelity diagnostic (needs the dense run)")
     ap.add_argument("--no-selectors", action="store_true",
@@ -376,9 +383,14 @@ def main() -> int:
     def mask_step():
         nb.nabla_build_mask(q, k, thr, w.sta_struct(), out=lists, workspace=ws_mask, stream=stream)
 
-    def fwd_step():
+    # Scheduling hint: blocks per latent frame (the block order of section 3.1.1);
+    # outputs are bitwise identical with or without it.
+    fb = 0 if args.no_pairs else (w.Hs // w.P) * (w.Ws // w.P)
+
+    def fwd_step(frame_blocks=None):
         nb.nabla_sparse_attn_fwd(q, k, v, lists["kv_count"], lists["kv_idx"], o=o, lse=lse,
-                                 workspace=ws_fwd, stream=stream)
+                                 workspace=ws_fwd, stream=stream,
+                                 frame_blocks=fb if frame_blocks is None else frame_blocks)
 
     for _ in range(args.warmup):
         mask_step()
@@ -410,6 +422,18 @@ def main() -> int:
     fwd_tflops = step_flops / (fwd_ms * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms (mask {mask_ms:.3f} ms, forward {fwd_ms:.3f} ms); "
         f"forward {fwd_tflops:.1f} TFLOP/s = {100 * fwd_tflops / PEAK_BF16_TFLOPS:.1f}% of peak")
+    # The one-block-per-workgroup forward on the same lists, for reference.
+    unpaired_ms = None
+    if fb:
+        e_u = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fwd_step(0)
+        e_u[0].record(stream)
+        for _ in range(5):
+            fwd_step(0)
+        e_u[1].record(stream)
+        torch.cuda.synchronize()
+        unpaired_ms = e_u[0].elapsed_time(e_u[1]) / 5
+        log(f"forward without the frame hint: {unpaired_ms:.3f} ms")
 
     # Mask stage algorithmic bytes: read Q and K once, write counts and lists.
     mask_bytes = 2 * B * H * S * D * 2 + 4 * B * H * n + 4 * kept
@@ -423,13 +447,13 @@ def main() -> int:
         dense_lists = {"kv_count": torch.empty_like(lists["kv_count"]), "kv_idx": torch.empty_like(lists["kv_idx"])}
         nb.nabla_build_mask(q, k, 1.0, out=dense_lists, workspace=ws_mask, stream=stream)
         nb.nabla_sparse_attn_fwd(q, k, v, dense_lists["kv_count"], dense_lists["kv_idx"], o=o, lse=lse,
-                                 workspace=ws_fwd, stream=stream)
+                                 workspace=ws_fwd, stream=stream, frame_blocks=fb)
         torch.cuda.synchronize()
         dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.dense_iters)]
         for i in range(args.dense_iters):
             dev_ev[i][0].record(stream)
             nb.nabla_sparse_attn_fwd(q, k, v, dense_lists["kv_count"], dense_lists["kv_idx"], o=o, lse=lse,
-                                     workspace=ws_fwd, stream=stream)
+                                     workspace=ws_fwd, stream=stream, frame_blocks=fb)
             dev_ev[i][1].record(stream)
         torch.cuda.synchronize()
         dense_ms = sum(e[0].elapsed_time(e[1]) for e in dev_ev) / args.dense_iters
@@ -488,10 +512,12 @@ def main() -> int:
             "B": B, "H": H, "S": S, "D": D, "N": w.N,
             "thr": round(thr, 6), "block_sparsity": round(sparsity, 5),
             "step": "nabla_build_mask + nabla_sparse_attn_fwd (inputs resident in HBM)",
+            "frame_blocks": fb,
         },
         "pct_of_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "forward_tflops": round(fwd_tflops, 2),
         "forward_ms": round(fwd_ms, 4),
+        "forward_unpaired_ms": round(unpaired_ms, 4) if unpaired_ms is not None else None,
         "mask_ms": round(mask_ms, 4),
         "mask_gbps": round(mask_gbps, 1),
         "mask_pct_hbm_peak": round(100 * mask_gbps / PEAK_HBM_GBPS, 2),
@@ -501,7 +527,7 @@ def main() -> int:
                                        if args.dense_iters > 0 else None),
         "linearity": round(speedup * (1 - sparsity), 3) if args.dense_iters > 0 else None,
         "roofline": {
-            "kernel": FWD_KERNEL,
+            "kernel": FWD_KERNEL if fb else "attn_fwd_kernel",
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -518,7 +544,7 @@ def main() -> int:
         # Top-k at the CDF rule's mean kept count; STA at Table 1's (18, 24, 24) window.
         topk = max(1, round(kept / (B * H * n)))
         result["selectors"] = selector_bench(w, q, k, v, lists, ws_mask, ws_fwd, o, lse, stream, 5,
-                                             topk, (18, 24, 24), mass)
+                                             topk, (18, 24, 24), mass, fb)
     if fidelity is not None:
         result["fidelity"] = fidelity
         del mass

@@ -91,7 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.nabla_sparse_attn_fwd.restype = ctypes.c_int
     lib.nabla_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
-                                          ctypes.c_float, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp]
+                                          ctypes.c_float, _i32, _vp, _i32, _vp, _vp, ctypes.c_size_t,
+                                          _vp]
     lib.nabla_sparse_attn_bwd.restype = ctypes.c_int
     lib.nabla_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
@@ -233,11 +234,13 @@ def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
                           o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                           want_lse: bool = True, out_dtype: torch.dtype = torch.bfloat16,
-                          workspace: Optional[torch.Tensor] = None,
+                          frame_blocks: int = 0, workspace: Optional[torch.Tensor] = None,
                           stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Block-sparse attention forward (eq. (4) on the kept blocks).
 
-    Returns (O, LSE fp32); O is bf16 or fp32 (``out_dtype``)."""
+    Returns (O, LSE fp32); O is bf16 or fp32 (``out_dtype``). ``frame_blocks``
+    (blocks per latent frame, (Hs/P)*(Ws/P)) lets query blocks i and i + F share
+    their K/V loads; results are identical with or without it."""
     _check_qkv("q", q)
     B, H, S, D = q.shape
     _check_qkv("k", k, q.shape)
@@ -261,8 +264,8 @@ def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     ws, size = _workspace(NABLA_OP_FWD, B, H, S, D, N, q.device, workspace)
     st = load_library().nabla_sparse_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), B, H, S, D, N, _ptr(kv_count), _ptr(kv_idx), scale, _ptr(o),
-        o_dtype, _ptr(lse) if want_lse else None, _ptr(ws), ws.numel(), _stream(q, stream))
+        _ptr(q), _ptr(k), _ptr(v), B, H, S, D, N, _ptr(kv_count), _ptr(kv_idx), scale,
+        int(frame_blocks), _ptr(o), o_dtype, _ptr(lse) if want_lse else None, _ptr(ws), ws.numel(), _stream(q, stream))
     if st != NABLA_OK:
         raise NablaError(st, "nabla_sparse_attn_fwd")
     return o, (lse if want_lse else None)

@@ -5,8 +5,7 @@
 // block attends only to the key blocks of its kept list. Online softmax over
 // the kept blocks (flash-attention style), bf16 MFMA with fp32 accumulation.
 //
-// Work item = one 64-row query block; workgroup = 2 waves of 32 query rows.
-// Per kept key block j:
+// A wave owns 32 query rows of one 64-row query block. Per kept key block j:
 //   S^T = K Q^T: A operand = K rows from LDS, B operand = Q^T in registers;
 //   O^T += V^T P^T: B operand = P^T straight from the S^T accumulators (their
 //   rows become the contraction slots), A operand = V^T read from the
@@ -18,6 +17,20 @@
 // reads, so global latency overlaps a whole block of compute. exp2 is used
 // with log2(e) folded into the scale, and the output is rescaled only when a
 // row maximum grows by more than 2^8.
+//
+// Two kernels share that per-block step:
+//   attn_fwd_kernel       one query block per workgroup (2 waves);
+//   attn_fwd_pair_kernel  two query blocks per workgroup (4 waves): the same
+//                         tile position in two consecutive frames (blocks i
+//                         and i + F in the block order of section 3.1.1),
+//                         whose kept lists overlap strongly. The workgroup
+//                         walks the ascending union of both lists, loads each
+//                         K/V tile once, and each pair of waves computes only
+//                         the blocks of its own list -- in the same order as
+//                         the single kernel, so the results are bitwise equal.
+// The forward is bound by K/V tile traffic from beyond L2 (each kept pair
+// reads a 32 KB tile pair); sharing tiles between the two blocks of a pair
+// removes the loads of their common blocks.
 
 #include "common.h"
 #include "kernels.h"
@@ -36,8 +49,169 @@ struct Tile {
     static constexpr int CPR = D / 8;            // 16-byte chunks per row
     static constexpr int KSTB = 2 * D + 16;      // K row stride (bytes): 16-byte pad
     static constexpr int VSTB = 2 * D + 64;      // V row stride (bytes): 64-byte pad
-    static constexpr int LOADS = kBlockN * CPR / 128;  // 16-byte chunks per thread per tile
+    static constexpr int CHUNKS = kBlockN * CPR; // 16-byte chunks per tile
 };
+
+// Per-wave state of 32 query rows.
+template <int D>
+struct RowState {
+    static constexpr int KK = D / 16;  // MFMA k-steps over the head dimension
+    static constexpr int DT = D / 32;  // 32-row d tiles of O^T
+    bf16x8_t qf[KK];                   // Q^T as the B operand
+    f32x16_t oacc[DT];                 // O^T accumulators
+    // m_run: running maximum (log2 units); l_run: sum of fp32 probabilities
+    // (for LSE); w_run: sum of the bf16-rounded probabilities that feed the PV
+    // product (the output's normaliser).
+    float m_run, l_run, w_run;
+};
+
+// Lane l of a wave: query column c = l % 32, half h = l / 32.
+template <int D>
+__device__ __forceinline__ void load_rows(RowState<D>& st, const uint16_t* qrow_ptr, int h) {
+#pragma unroll
+    for (int kk = 0; kk < RowState<D>::KK; ++kk)
+        st.qf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow_ptr + 16 * kk + 8 * h));
+#pragma unroll
+    for (int t = 0; t < RowState<D>::DT; ++t) st.oacc[t] = zero16();
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+    st.w_run = 0.f;
+}
+
+// One kept key block: K tile at kbase (lane base for the S^T A operand), V
+// tile at vbase (lane base for the transposing V^T reads).
+template <int D>
+__device__ __forceinline__ void block_step(RowState<D>& st, const char* kbase, const char* vbase,
+                                           float scale_log2) {
+    using T = Tile<D>;
+    constexpr int KK = RowState<D>::KK, DT = RowState<D>::DT;
+    const uint32_t ones_bf16x2 = 0x3f803f80u;
+
+    // S^T (64 keys x 32 queries) as two 32 x 32 tiles; A fragments read first.
+    f32x16_t s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        bf16x8_t a[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + 32 * kt * T::KSTB + 32 * kk));
+        s[kt] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s[kt] = mfma_32x32x16(a[kk], st.qf[kk], s[kt]);
+    }
+
+    // Online softmax for query column c (keys split over this lane and lane ^ 32).
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[1][r]);
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    // Rescale only when some row's maximum grew by more than 2^8; otherwise
+    // keep the old reference (probabilities then stay below 2^8).
+    const bool grow = mx > st.m_run + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : st.m_run;
+        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+        st.l_run *= alpha;
+        st.w_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[t][r] *= alpha;
+        st.m_run = m_new;
+    }
+    float rs = 0.f, ws = 0.f;
+    uint32_t pw[2][8];  // bf16 probabilities, B operands of the PV product
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(s[kt][2 * e] * scale_log2 - st.m_run);
+            const float p1 = __builtin_amdgcn_exp2f(s[kt][2 * e + 1] * scale_log2 - st.m_run);
+            rs += p0 + p1;
+            pw[kt][e] = pack_bf16x2(p0, p1);
+            ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[kt][e]),
+                                                 __builtin_bit_cast(bf16x2_t, ones_bf16x2), ws,
+                                                 false);
+        }
+    rs += __shfl_xor(rs, 32);
+    ws += __shfl_xor(ws, 32);
+    st.l_run += rs;
+    st.w_run += ws;
+
+    // O^T += V^T P^T. For key tile kt and half u, B = S^T registers 8u..8u+7:
+    // slot s is key 32kt + 16u + 8*(s/4) + 4h + s%4; the transposing reads
+    // of rows 32kt + 16u + {0, 8} + 4h + jj deliver V^T with the same map.
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8_t b = as_bf16x8(make_uint4(pw[kt][4 * u], pw[kt][4 * u + 1],
+                                                    pw[kt][4 * u + 2], pw[kt][4 * u + 3]));
+            const char* vrow = vbase + (32 * kt + 16 * u) * T::VSTB;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16_t*)(vrow + 64 * t));
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16_t*)(vrow + 8 * T::VSTB + 64 * t));
+                const uint2 ulo = __builtin_bit_cast(uint2, lo);
+                const uint2 uhi = __builtin_bit_cast(uint2, hi);
+                st.oacc[t] = mfma_32x32x16(as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y)), b,
+                                           st.oacc[t]);
+            }
+        }
+}
+
+// Epilogue: O[query][d] = O^T[d][query] / w. The lane holds query row `qrow`
+// and d = 32t + 8g + 4h + e for register 4g + e of tile t.
+template <int D>
+__device__ __forceinline__ void store_rows(const RowState<D>& st, int64_t head, int64_t qrow, int h,
+                                           void* __restrict__ o, int o_fp32, float* __restrict__ lse,
+                                           int64_t lse_index) {
+    constexpr int DT = RowState<D>::DT;
+    const float inv_l = st.w_run > 0.f ? 1.0f / st.w_run : 0.f;
+    if (o_fp32) {
+        float* orow = static_cast<float*>(o) + head + qrow * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4*>(orow + 32 * t + 8 * g + 4 * h) =
+                    make_float4(st.oacc[t][4 * g + 0] * inv_l, st.oacc[t][4 * g + 1] * inv_l,
+                                st.oacc[t][4 * g + 2] * inv_l, st.oacc[t][4 * g + 3] * inv_l);
+    } else {
+        uint16_t* orow = static_cast<uint16_t*>(o) + head + qrow * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint2 w;
+                w.x = pack_bf16x2(st.oacc[t][4 * g + 0] * inv_l, st.oacc[t][4 * g + 1] * inv_l);
+                w.y = pack_bf16x2(st.oacc[t][4 * g + 2] * inv_l, st.oacc[t][4 * g + 3] * inv_l);
+                *reinterpret_cast<uint2*>(orow + 32 * t + 8 * g + 4 * h) = w;
+            }
+    }
+    if (lse && h == 0)
+        lse[lse_index] = st.l_run > 0.f ? (st.m_run + __log2f(st.l_run)) * kLn2 : -INFINITY;
+}
+
+// Lane bases for LDS reads (everything else is an immediate offset).
+// K rows for the S^T A operand: row 32 kt + c, bytes 32 kk + 16 h.
+template <int D>
+__device__ __forceinline__ const char* k_lane_base(const char* sK, int lane) {
+    return sK + (lane & 31) * Tile<D>::KSTB + 16 * (lane >> 5);
+}
+// V^T via the transposing read: this lane supplies the address of row
+// rbase + 4h + (lane % 16) / 4, columns 32 dt + 16 ((lane / 16) % 2) +
+// 4 (lane % 4) .. +3, and receives V[rbase + 4h + jj][32 dt + lane % 32]
+// for jj = 0..3 (rbase = 32 kt + 16 u, plus 8 for the upper four slots).
+template <int D>
+__device__ __forceinline__ const char* v_lane_base(const char* sV, int lane) {
+    return sV + (4 * (lane >> 5) + ((lane & 15) >> 2)) * Tile<D>::VSTB +
+           2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+}
 
 }  // namespace
 
@@ -48,9 +222,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ order, XcdSchedule sched,
     float scale_log2, void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
     using T = Tile<D>;
-    constexpr int KK = D / 16;  // MFMA k-steps over the head dimension
-    constexpr int DT = D / 32;  // 32-row d tiles of O^T
-    constexpr int L = T::LOADS;
+    constexpr int L = T::CHUNKS / 128;  // 16-byte chunks per thread per tile
     __shared__ __attribute__((aligned(16))) char sK[kBlockN * T::KSTB];
     __shared__ __attribute__((aligned(16))) char sV[kBlockN * T::VSTB];
 
@@ -68,12 +240,9 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
     const uint16_t* kh = k + head;
     const uint16_t* vh = v + head;
 
-    // Q^T as the B operand: lane holds query (wave*32 + c), d = 16*kk + 8*h + 0..7.
-    const int qrow = qb * kBlockN + wave * 32 + c;
-    bf16x8_t qf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-        qf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(q + head + (int64_t)qrow * D + 16 * kk + 8 * h));
+    const int64_t qrow = (int64_t)qb * kBlockN + wave * 32 + c;
+    RowState<D> st;
+    load_rows<D>(st, q + head + qrow * D, h);
 
     // Staging: thread chunk e = tid + 128 i covers row e / CPR, chunk e % CPR.
     u32x4_t kr[L], vr[L];
@@ -98,23 +267,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
         }                                                                      \
     } while (0)
 
-    // Lane bases for LDS reads (everything else is an immediate offset).
-    // K rows for the S^T A operand: row 32 kt + c, bytes 32 kk + 16 h.
-    const char* kbase = sK + c * T::KSTB + 16 * h;
-    // V^T via the transposing read: this lane supplies the address of row
-    // rbase + 4h + (lane % 16) / 4, columns 32 dt + 16 ((lane / 16) % 2) +
-    // 4 (lane % 4) .. +3, and receives V[rbase + 4h + jj][32 dt + lane % 32]
-    // for jj = 0..3 (rbase = 32 kt + 16 u, plus 8 for the upper four slots).
-    const char* vbase = sV + (4 * h + ((lane & 15) >> 2)) * T::VSTB +
-                        2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-
-    f32x16_t oacc[DT];
-#pragma unroll
-    for (int t = 0; t < DT; ++t) oacc[t] = zero16();
-    // l_run: sum of fp32 probabilities (for LSE); w_run: sum of the bf16-rounded
-    // probabilities that feed the PV product (the output's normaliser).
-    float m_run = -INFINITY, l_run = 0.f, w_run = 0.f;
-    const uint32_t ones_bf16x2 = 0x3f803f80u;
+    const char* kbase = k_lane_base<D>(sK, lane);
+    const char* vbase = v_lane_base<D>(sV, lane);
 
     if (cnt > 0) {
         NABLA_FETCH(0);
@@ -123,81 +277,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
         __syncthreads();
     }
     for (int it = 0; it < cnt; ++it) {
-        // S^T (64 keys x 32 queries) as two 32 x 32 tiles; A fragments read first.
-        f32x16_t s[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            bf16x8_t a[KK];
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + 32 * kt * T::KSTB + 32 * kk));
-            s[kt] = zero16();
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s[kt] = mfma_32x32x16(a[kk], qf[kk], s[kt]);
-        }
-
-        // Online softmax for query column c (keys split over this lane and lane ^ 32).
-        float mx = s[0][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[1][r]);
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-        // Rescale only when some row's maximum grew by more than 2^8; otherwise
-        // keep the old reference (probabilities then stay below 2^8).
-        const bool grow = mx > m_run + kRescaleLog2;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-            const float m_new = grow ? mx : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-            w_run *= alpha;
-#pragma unroll
-            for (int t = 0; t < DT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-            m_run = m_new;
-        }
-        float rs = 0.f, ws = 0.f;
-        uint32_t pw[2][8];  // bf16 probabilities, B operands of the PV product
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(s[kt][2 * e] * scale_log2 - m_run);
-                const float p1 = __builtin_amdgcn_exp2f(s[kt][2 * e + 1] * scale_log2 - m_run);
-                rs += p0 + p1;
-                pw[kt][e] = pack_bf16x2(p0, p1);
-                ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[kt][e]),
-                                                     __builtin_bit_cast(bf16x2_t, ones_bf16x2), ws,
-                                                     false);
-            }
-        rs += __shfl_xor(rs, 32);
-        ws += __shfl_xor(ws, 32);
-        l_run += rs;
-        w_run += ws;
-
-        // O^T += V^T P^T. For key tile kt and half u, B = S^T registers 8u..8u+7:
-        // slot s is key 32kt + 16u + 8*(s/4) + 4h + s%4; the transposing reads
-        // of rows 32kt + 16u + {0, 8} + 4h + jj deliver V^T with the same map.
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8_t b = as_bf16x8(make_uint4(pw[kt][4 * u], pw[kt][4 * u + 1],
-                                                        pw[kt][4 * u + 2], pw[kt][4 * u + 3]));
-                const char* vrow = vbase + (32 * kt + 16 * u) * T::VSTB;
-#pragma unroll
-                for (int t = 0; t < DT; ++t) {
-                    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_v4i16_t*)(vrow + 64 * t));
-                    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_v4i16_t*)(vrow + 8 * T::VSTB + 64 * t));
-                    const uint2 ulo = __builtin_bit_cast(uint2, lo);
-                    const uint2 uhi = __builtin_bit_cast(uint2, hi);
-                    oacc[t] = mfma_32x32x16(as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y)), b,
-                                            oacc[t]);
-                }
-            }
+        block_step<D>(st, kbase, vbase, scale_log2);
         if (it + 1 < cnt) {
             __syncthreads();  // every wave has read K_j and V_j
             NABLA_STAGE();  // block it+1, fetched one iteration ago
@@ -208,34 +288,162 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
 
 #undef NABLA_FETCH
 #undef NABLA_STAGE
-
-    // Epilogue: O[query][d] = O^T[d][query] / w. This lane holds query (wave*32 + c)
-    // and d = 32t + 8g + 4h + e for register 4g + e of tile t.
-    const float inv_l = w_run > 0.f ? 1.0f / w_run : 0.f;
-    if (o_fp32) {
-        float* orow = static_cast<float*>(o) + head + (int64_t)qrow * D;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<float4*>(orow + 32 * t + 8 * g + 4 * h) =
-                    make_float4(oacc[t][4 * g + 0] * inv_l, oacc[t][4 * g + 1] * inv_l,
-                                oacc[t][4 * g + 2] * inv_l, oacc[t][4 * g + 3] * inv_l);
-    } else {
-        uint16_t* orow = static_cast<uint16_t*>(o) + head + (int64_t)qrow * D;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint2 w;
-                w.x = pack_bf16x2(oacc[t][4 * g + 0] * inv_l, oacc[t][4 * g + 1] * inv_l);
-                w.y = pack_bf16x2(oacc[t][4 * g + 2] * inv_l, oacc[t][4 * g + 3] * inv_l);
-                *reinterpret_cast<uint2*>(orow + 32 * t + 8 * g + 4 * h) = w;
-            }
-    }
-    if (lse && h == 0)
-        lse[bh * (int64_t)S + qrow] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    store_rows<D>(st, head, qrow, h, o, o_fp32, lse, bh * (int64_t)S + qrow);
 }
+
+// Two query blocks per workgroup: waves 0-1 serve block A, waves 2-3 block B
+// (B = A + F, the same tile in the next frame; -1 when A is in the last frame
+// of an odd frame count). The workgroup walks the ascending union of the two
+// kept lists with two cursors: `cur` for the block being computed, `pre` two
+// union steps ahead for the prefetch. Each union step carries two flags (in
+// A's list, in B's list); a pair of waves computes a step only if its flag is
+// set, so each block sees exactly its own kept blocks in ascending order.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int S, int n, int F, const int32_t* __restrict__ kv_count,
+    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ order, XcdSchedule sched,
+    float scale_log2, void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
+    using T = Tile<D>;
+    constexpr int L = T::CHUNKS / 256;  // 16-byte chunks per thread per tile
+    __shared__ __attribute__((aligned(16))) char sK[kBlockN * T::KSTB];
+    __shared__ __attribute__((aligned(16))) char sV[kBlockN * T::VSTB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 1;  // 0: block A, 1: block B
+    const int h = lane >> 5, c = lane & 31;
+    const int64_t pair = scheduled_item(sched, order, blockIdx.x);
+    if (pair < 0) return;  // padding slot (whole workgroup)
+    // Pair p of a head: frames 2s and 2s+1 of tile position tp.
+    const int np = sched.n;
+    const int64_t bh = pair / np;
+    const int p = (int)(pair % np);
+    const int s2 = 2 * (p / F), tp = p % F;
+    const int qa = s2 * F + tp;
+    const int qbB = qa + F < n ? qa + F : -1;
+    const int64_t itemA = bh * (int64_t)n + qa;
+    const int64_t itemB = bh * (int64_t)n + (qbB < 0 ? qa : qbB);
+    int cntA = kv_count[itemA];
+    cntA = cntA < 0 ? 0 : (cntA > n ? n : cntA);
+    int cntB = qbB < 0 ? 0 : kv_count[itemB];
+    cntB = cntB < 0 ? 0 : (cntB > n ? n : cntB);
+    const int32_t* listA = kv_idx + itemA * (int64_t)n;
+    const int32_t* listB = kv_idx + itemB * (int64_t)n;
+    const int64_t head = bh * (int64_t)S * D;
+    const uint16_t* kh = k + head;
+    const uint16_t* vh = v + head;
+
+    const int my_qb = grp ? qbB : qa;
+    const bool active = my_qb >= 0;
+    const int64_t qrow = (int64_t)(active ? my_qb : qa) * kBlockN + (wave & 1) * 32 + c;
+    RowState<D> st;
+    load_rows<D>(st, q + head + qrow * D, h);
+
+    // Union cursor: positions in both lists; the next element of each (n = end).
+    struct Cursor {
+        int ia, ib;
+    };
+    auto entry = [&](const int32_t* list, int i, int cntL) -> int {
+        if (i >= cntL) return n;
+        const int j = list[i];
+        return (unsigned)j < (unsigned)n ? j : 0;
+    };
+    // Advance a cursor by one union step; returns the block and its flags.
+    auto step = [&](Cursor& cu, int& j, int& flags) {
+        const int ja = entry(listA, cu.ia, cntA);
+        const int jb = entry(listB, cu.ib, cntB);
+        j = ja < jb ? ja : jb;
+        flags = (ja == j ? 1 : 0) | (jb == j ? 2 : 0);
+        cu.ia += (flags & 1);
+        cu.ib += (flags & 2) >> 1;
+    };
+
+    u32x4_t kr[L], vr[L];
+#define NABLA_PFETCH(J)                                                        \
+    do {                                                                       \
+        const int64_t off_ = (int64_t)(J) * kBlockN * D;                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < L; ++i_) {                     \
+            const int e_ = tid + 256 * i_;                                     \
+            kr[i_] = *reinterpret_cast<const u32x4_t*>(kh + off_ + e_ * 8);    \
+            vr[i_] = *reinterpret_cast<const u32x4_t*>(vh + off_ + e_ * 8);    \
+        }                                                                      \
+    } while (0)
+#define NABLA_PSTAGE()                                                         \
+    do {                                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < L; ++i_) {                     \
+            const int e_ = tid + 256 * i_;                                     \
+            const int r_ = e_ / T::CPR, ch_ = e_ % T::CPR;                     \
+            *reinterpret_cast<u32x4_t*>(sK + r_ * T::KSTB + 16 * ch_) = kr[i_];\
+            *reinterpret_cast<u32x4_t*>(sV + r_ * T::VSTB + 16 * ch_) = vr[i_];\
+        }                                                                      \
+    } while (0)
+
+    const char* kbase = k_lane_base<D>(sK, lane);
+    const char* vbase = v_lane_base<D>(sV, lane);
+
+    // Union length: |A| + |B| - |A and B|, counted by walking the cursor.
+    Cursor pre{0, 0};
+    int f_cur = 0, f_next = 0;  // flags of the staged step and of the step in flight
+    int j_tmp;
+    if (cntA + cntB > 0) {
+        step(pre, j_tmp, f_cur);
+        NABLA_PFETCH(j_tmp);
+        NABLA_PSTAGE();
+        if (pre.ia < cntA || pre.ib < cntB) {
+            step(pre, j_tmp, f_next);
+            NABLA_PFETCH(j_tmp);
+        }
+        __syncthreads();
+        for (;;) {
+            const int mine = grp ? (f_cur & 2) : (f_cur & 1);
+            if (mine && active) block_step<D>(st, kbase, vbase, scale_log2);
+            if (f_next == 0) break;  // the computed step was the last one
+            __syncthreads();  // every wave is done with the staged tiles
+            NABLA_PSTAGE();   // the step fetched one iteration ago
+            f_cur = f_next;
+            f_next = 0;
+            if (pre.ia < cntA || pre.ib < cntB) {
+                step(pre, j_tmp, f_next);
+                NABLA_PFETCH(j_tmp);
+            }
+            __syncthreads();
+        }
+    }
+
+#undef NABLA_PFETCH
+#undef NABLA_PSTAGE
+    if (active) store_rows<D>(st, head, qrow, h, o, o_fp32, lse, bh * (int64_t)S + qrow);
+}
+
+namespace {
+
+constexpr int kPairThreads = 256;
+
+// Work of pair p of head bh (frames 2s, 2s+1 of tile position p % F): the mean
+// of the two kept counts, in [0, n], as the longest-first key.
+__global__ __launch_bounds__(kPairThreads) void pair_counts_kernel(const int32_t* __restrict__ kv_count,
+                                                                   int n, int F, int np,
+                                                                   int64_t total,
+                                                                   int32_t* __restrict__ pc) {
+    const int64_t g = (int64_t)blockIdx.x * kPairThreads + threadIdx.x;
+    if (g >= total) return;
+    const int64_t bh = g / np;
+    const int p = (int)(g % np);
+    const int qa = 2 * (p / F) * F + p % F;
+    int a = kv_count[bh * n + qa];
+    a = a < 0 ? 0 : (a > n ? n : a);
+    int b = 0;
+    if (qa + F < n) {
+        b = kv_count[bh * n + qa + F];
+        b = b < 0 ? 0 : (b > n ? n : b);
+    }
+    pc[g] = (a + b + 1) / 2;
+}
+
+}  // namespace
+
+int pair_count(int n, int F) { return F * ((n / F + 1) / 2); }
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t BH, int S, int D,
                            const int32_t* kv_count, const int32_t* kv_idx, const int32_t* order,
@@ -251,6 +459,34 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
     else
         attn_fwd_kernel<64><<<grid, 128, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, S, n, kv_count, kv_idx,
+            order, sched, sl2, o, o_fp32 ? 1 : 0, lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_pair_counts(const int32_t* kv_count, int64_t BH, int n, int F, int32_t* pc,
+                              hipStream_t stream) {
+    const int np = pair_count(n, F);
+    const int64_t total = BH * np;
+    const unsigned grid = (unsigned)((total + kPairThreads - 1) / kPairThreads);
+    pair_counts_kernel<<<grid, kPairThreads, 0, stream>>>(kv_count, n, F, np, total, pc);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_pairs(const void* q, const void* k, const void* v, int64_t BH, int S,
+                                 int D, int F, const int32_t* kv_count, const int32_t* kv_idx,
+                                 const int32_t* order, const XcdSchedule& sched,
+                                 float softmax_scale, void* o, bool o_fp32, float* lse,
+                                 hipStream_t stream) {
+    const int n = S / kBlockN;
+    const unsigned grid = (unsigned)sched.grid;
+    const float sl2 = softmax_scale * kLog2e;
+    if (D == 128)
+        attn_fwd_pair_kernel<128><<<grid, 256, 0, stream>>>(
+            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, S, n, F, kv_count, kv_idx,
+            order, sched, sl2, o, o_fp32 ? 1 : 0, lse);
+    else
+        attn_fwd_pair_kernel<64><<<grid, 256, 0, stream>>>(
+            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, S, n, F, kv_count, kv_idx,
             order, sched, sl2, o, o_fp32 ? 1 : 0, lse);
     return hipGetLastError();
 }

@@ -30,10 +30,11 @@ hipError_t launch_select(int mode, const float* logits, int64_t BH, int n, int k
 hipError_t launch_transpose(const uint32_t* bits, int64_t BH, int n, int words_per_row,
                             int32_t* q_count, int32_t* q_idx, hipStream_t stream);
 
-// Per-head longest-first order: order[h*n + p] = item id (h*n + i) of head h's
-// p-th item, counts descending (ties in any order).
-hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int n, int32_t* order,
-                            hipStream_t stream);
+// Per-head longest-first order over `items` items per head whose counts lie in
+// [0, maxc] (maxc <= NABLA_MAX_BLOCKS; others are clamped): order[h*items + p] =
+// item id (h*items + i) of head h's p-th item, counts descending (ties in any order).
+hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int items, int maxc,
+                            int32_t* order, hipStream_t stream);
 
 // XCD-aware launch geometry (see schedule.hip): heads are split into `parts`
 // interleaved shares so that `units` = BH * parts is a multiple of the 8 XCDs;
@@ -71,6 +72,17 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
                            const XcdSchedule& sched,
                            float softmax_scale, void* o, bool o_fp32, float* lse,
                            hipStream_t stream);
+
+// Paired forward (attn_fwd_pair_kernel): pairs of query blocks (i, i + F), F =
+// blocks per frame; pair_count(n, F) pairs per head (n % F == 0).
+int pair_count(int n, int F);
+hipError_t launch_pair_counts(const int32_t* kv_count, int64_t BH, int n, int F, int32_t* pc,
+                              hipStream_t stream);
+hipError_t launch_attn_fwd_pairs(const void* q, const void* k, const void* v, int64_t BH, int S,
+                                 int D, int F, const int32_t* kv_count, const int32_t* kv_idx,
+                                 const int32_t* order, const XcdSchedule& sched,
+                                 float softmax_scale, void* o, bool o_fp32, float* lse,
+                                 hipStream_t stream);
 
 hipError_t launch_bwd_delta(const void* o, bool o_fp32, const void* d_o, int64_t rows, int D,
                             float* delta, hipStream_t stream);

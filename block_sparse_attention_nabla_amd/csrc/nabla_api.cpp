@@ -146,8 +146,9 @@ nabla_status_t nabla_build_sta_mask(int32_t B, int32_t H, int32_t S, int32_t N,
 nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t B,
                                      int32_t H, int32_t S, int32_t D, int32_t N,
                                      const int32_t* kv_count, const int32_t* kv_idx,
-                                     float softmax_scale, void* o, int32_t o_dtype, float* lse,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+                                     float softmax_scale, int32_t frame_blocks, void* o,
+                                     int32_t o_dtype, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
     Shape s;
     nabla_status_t st = check_shape(B, H, S, D, N, &s);
     if (st != NABLA_OK) return st;
@@ -155,15 +156,29 @@ nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return NABLA_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || isinf(softmax_scale)) return NABLA_ERR_INVALID_ARG;
     if (o_dtype != NABLA_DTYPE_BF16 && o_dtype != NABLA_DTYPE_FP32) return NABLA_ERR_INVALID_ARG;
+    if (frame_blocks < 0 || (frame_blocks > 0 && s.n % frame_blocks != 0)) return NABLA_ERR_INVALID_ARG;
     const FwdWorkspace w = fwd_workspace(s);
     if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
 
     int32_t* order = reinterpret_cast<int32_t*>(ws_at(workspace, w.order));
     hipStream_t hs = as_stream(stream);
-    const XcdSchedule sched = make_schedule(s.BH, (int)s.n);
-    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, (int)s.n, order, hs));
+    const bool o_fp32 = o_dtype == NABLA_DTYPE_FP32;
+    const int n = (int)s.n;
+    if (frame_blocks > 0 && n / frame_blocks >= 2) {
+        // Pairs of query blocks (i, i + F): the same tile in consecutive frames.
+        const int np = pair_count(n, frame_blocks);
+        int32_t* pc = reinterpret_cast<int32_t*>(ws_at(workspace, w.counts));
+        const XcdSchedule sched = make_schedule(s.BH, np);
+        NABLA_LAUNCH(launch_pair_counts(kv_count, s.BH, n, frame_blocks, pc, hs));
+        NABLA_LAUNCH(launch_lpt_order(pc, s.BH, np, n, order, hs));
+        NABLA_LAUNCH(launch_attn_fwd_pairs(q, k, v, s.BH, (int)s.S, (int)s.D, frame_blocks, kv_count,
+                                           kv_idx, order, sched, softmax_scale, o, o_fp32, lse, hs));
+        return NABLA_OK;
+    }
+    const XcdSchedule sched = make_schedule(s.BH, n);
+    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, n, n, order, hs));
     NABLA_LAUNCH(launch_attn_fwd(q, k, v, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx, order, sched,
-                                 softmax_scale, o, o_dtype == NABLA_DTYPE_FP32, lse, hs));
+                                 softmax_scale, o, o_fp32, lse, hs));
     return NABLA_OK;
 }
 
@@ -194,10 +209,10 @@ nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v
     hipStream_t hs = as_stream(stream);
     NABLA_LAUNCH(launch_bwd_delta(o, o_dtype == NABLA_DTYPE_FP32, d_o, s.BH * s.S, (int)s.D, delta, hs));
     const XcdSchedule sched = make_schedule(s.BH, (int)s.n);
-    NABLA_LAUNCH(launch_lpt_order(q_count, s.BH, (int)s.n, order_kv, hs));
+    NABLA_LAUNCH(launch_lpt_order(q_count, s.BH, (int)s.n, (int)s.n, order_kv, hs));
     NABLA_LAUNCH(launch_bwd_dkdv(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, q_count, q_idx,
                                  order_kv, sched, softmax_scale, dk, dv, hs));
-    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, (int)s.n, order_q, hs));
+    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, (int)s.n, (int)s.n, order_q, hs));
     NABLA_LAUNCH(launch_bwd_dq(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx,
                                order_q, sched, softmax_scale, dq, hs));
     return NABLA_OK;

@@ -20,19 +20,20 @@ namespace nabla {
 
 constexpr int kLptThreads = 1024;
 
-// One workgroup per head: counting sort of the head's n items by count
-// (descending). order[h*n + p] = global item id of the head's p-th item.
+// One workgroup per head: counting sort of the head's `items` items by count
+// (descending; counts clamped to [0, n]). order[h*items + p] = global item id
+// of the head's p-th item.
 __global__ __launch_bounds__(kLptThreads) void head_lpt_kernel(const int32_t* __restrict__ counts,
-                                                               int n,
+                                                               int items, int n,
                                                                int32_t* __restrict__ order) {
     __shared__ int hist[NABLA_MAX_BLOCKS + 1];
     __shared__ int chunk_sum[kLptThreads];
     const int t = threadIdx.x;
-    const int64_t base = (int64_t)blockIdx.x * n;
+    const int64_t base = (int64_t)blockIdx.x * items;
     const int nb = n + 1;  // count values 0..n
     for (int c = t; c < nb; c += kLptThreads) hist[c] = 0;
     __syncthreads();
-    for (int it = t; it < n; it += kLptThreads) {
+    for (int it = t; it < items; it += kLptThreads) {
         int c = counts[base + it];
         c = c < 0 ? 0 : (c > n ? n : c);
         atomicAdd(&hist[c], 1);
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kLptThreads) void head_lpt_kernel(const int32_t* __
         run += hc;
     }
     __syncthreads();
-    for (int it = t; it < n; it += kLptThreads) {
+    for (int it = t; it < items; it += kLptThreads) {
         int c = counts[base + it];
         c = c < 0 ? 0 : (c > n ? n : c);
         const int pos = atomicAdd(&hist[c], 1);
@@ -67,9 +68,9 @@ __global__ __launch_bounds__(kLptThreads) void head_lpt_kernel(const int32_t* __
     }
 }
 
-hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int n, int32_t* order,
-                            hipStream_t stream) {
-    head_lpt_kernel<<<(unsigned)BH, kLptThreads, 0, stream>>>(counts, n, order);
+hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int items, int maxc,
+                            int32_t* order, hipStream_t stream) {
+    head_lpt_kernel<<<(unsigned)BH, kLptThreads, 0, stream>>>(counts, items, maxc, order);
     return hipGetLastError();
 }
 

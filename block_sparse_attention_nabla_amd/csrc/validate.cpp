@@ -57,7 +57,8 @@ StaWorkspace sta_workspace(const Shape& s) {
 FwdWorkspace fwd_workspace(const Shape& s) {
     FwdWorkspace w;
     w.order = 0;
-    w.total = align256((size_t)s.BH * s.n * sizeof(int32_t));
+    w.counts = align256((size_t)s.BH * s.n * sizeof(int32_t));
+    w.total = w.counts + align256((size_t)s.BH * s.n * sizeof(int32_t));
     return w;
 }
 

@@ -23,7 +23,7 @@ struct StaWorkspace {
     int words_per_row;
 };
 struct FwdWorkspace {
-    size_t order, total;
+    size_t order, counts, total;
 };
 struct BwdWorkspace {
     size_t delta, order_q, order_kv, total;

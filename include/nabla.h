@@ -145,12 +145,21 @@ NABLA_API nabla_status_t nabla_build_sta_mask(int32_t B, int32_t H, int32_t S, i
  * bf16 and divides by the sum of those rounded weights; LSE uses the fp32 sum.
  * Kept-block indices must lie in [0, n) and counts in [0, n]; a row with
  * count 0 yields O = 0 and LSE = -inf. bf16 MFMA, fp32 accumulation and softmax.
+ * frame_blocks (F) is a scheduling hint, 0 = none: the number of consecutive
+ * blocks that make up one latent frame in the block order of section 3.1.1
+ * (Figure 3), i.e. (Hs/P) * (Ws/P). With F > 0 (n % F == 0, else
+ * NABLA_ERR_INVALID_ARG) and at least two frames, query blocks i and i + F --
+ * the same tile position in consecutive frames, whose kept lists overlap
+ * strongly in video latents -- share one workgroup that loads each K/V tile of
+ * the union of their lists once. Outputs are bitwise identical either way
+ * (every query block still visits its own kept blocks in ascending order).
  */
 NABLA_API nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t B,
                                      int32_t H, int32_t S, int32_t D, int32_t N,
                                      const int32_t* kv_count, const int32_t* kv_idx,
-                                     float softmax_scale, void* o, int32_t o_dtype, float* lse,
-                                     void* workspace, size_t workspace_bytes, void* stream);
+                                     float softmax_scale, int32_t frame_blocks, void* o,
+                                     int32_t o_dtype, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /*
  * Block-sparse attention backward: gradients of the forward with the mask held

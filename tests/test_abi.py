@@ -106,8 +106,8 @@ def test_build_mask_sta_validation(lib):
 def test_fwd_validation(lib):
     f = lib.nabla_sparse_attn_fwd
 
-    def call(S=1024, D=64, scale=0.125, v=P, o=P, odt=0, ws=P2, wsb=BIG):
-        return f(P, P, v, 1, 2, S, D, 64, P, P, scale, o, odt, None, ws, wsb, None)
+    def call(S=1024, D=64, scale=0.125, v=P, o=P, odt=0, ws=P2, wsb=BIG, fb=0):
+        return f(P, P, v, 1, 2, S, D, 64, P, P, scale, fb, o, odt, None, ws, wsb, None)
 
     assert call(S=1000) == INVALID
     assert call(D=256) == UNSUPPORTED
@@ -117,6 +117,8 @@ def test_fwd_validation(lib):
     assert call(v=None) == INVALID
     assert call(o=None) == INVALID
     assert call(odt=2) == INVALID
+    assert call(fb=-1) == INVALID
+    assert call(fb=5) == INVALID        # n = 16 blocks is not a multiple of 5
     assert call(ws=None) == WORKSPACE
     assert call(wsb=4) == WORKSPACE
 

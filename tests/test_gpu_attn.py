@@ -142,6 +142,61 @@ def test_fwd_is_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+# Paired forward (frame_blocks = F): query blocks i and i + F share one workgroup.
+# Every block still visits its own kept blocks in ascending order with the same
+# arithmetic, so the outputs must equal the unpaired kernel's bit for bit.
+@pytest.mark.parametrize("name,F", [("tiny", 4), ("tiny", 1), ("dit_small", 16), ("dit_small_sta", 16)])
+def test_fwd_frame_pairs_bitwise_equal(name, F):
+    nb = _nb()
+    w = synth.get_workload(name)
+    x = synth.make_inputs(w)
+    q, k, v = (x[key].bfloat16().cuda() for key in ("q", "k", "v"))
+    assert F in (1, (w.Hs // w.P) * (w.Ws // w.P))
+    thr = 0.5 if name == "tiny" else w.thr_for(0.80)
+    lists = nb.nabla_build_mask(q, k, thr, w.sta_struct())
+    print(f"[fwd-pair] {name} F={F} n={w.n}", flush=True)
+    for out_dtype in (torch.bfloat16, torch.float32):
+        o0, l0 = nb.nabla_sparse_attn_fwd(q, k, v, lists["kv_count"], lists["kv_idx"], out_dtype=out_dtype)
+        o1, l1 = nb.nabla_sparse_attn_fwd(q, k, v, lists["kv_count"], lists["kv_idx"], out_dtype=out_dtype,
+                                          frame_blocks=F)
+        torch.cuda.synchronize()
+        assert torch.equal(o0.view(torch.int16) if out_dtype == torch.bfloat16 else o0.view(torch.int32),
+                           o1.view(torch.int16) if out_dtype == torch.bfloat16 else o1.view(torch.int32))
+        assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+
+
+def test_fwd_frame_pairs_edge_lists():
+    # Empty, single and identical lists, odd frame count (last frame unpaired),
+    # one partner empty: against the unpaired kernel (bitwise) and the oracle.
+    nb = _nb()
+    B, H, T, F = 1, 3, 5, 4
+    n = T * F
+    q, k, v, _ = _rand(B, H, 64 * n, 64, seed=21)
+    mask = _random_mask(B * H, n, 22, 0.25)
+    mask[0, 3] = 0                      # empty row, partner (7) non-empty
+    mask[1, 2] = mask[1, 6]             # identical partner lists
+    mask[2, 16:20] = 0                  # the unpaired last frame: empty rows
+    mask[2, 16, 3] = 1
+    mask[0, 9] = 0
+    mask[0, 13] = 0                     # both partners empty
+    lists = _lists_from_mask(mask, B, H)
+    o0, l0 = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"],
+                                      out_dtype=torch.float32)
+    o1, l1 = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"],
+                                      out_dtype=torch.float32, frame_blocks=F)
+    torch.cuda.synchronize()
+    assert torch.equal(o0.view(torch.int32), o1.view(torch.int32))
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+    keep = mask.copy()
+    ro, rlse = oracle.attn_fwd(q.float(), k.float(), v.float(), keep, 64)
+    got = o1.cpu().numpy().reshape(B * H, 64 * n, 64)
+    rows = keep.sum(axis=-1).repeat(64, axis=-1) > 0
+    e = attn_errors(got[rows], ro[rows])
+    assert e["max_abs"] <= O_MAX_ABS and e["mean_abs"] <= O_MEAN_ABS, e
+    assert (got[~rows] == 0).all()
+    assert torch.isneginf(l1.cpu().reshape(B * H, 64 * n)[torch.from_numpy(~rows)]).all()
+
+
 # ------------------------------------------------------------------ backward
 def _bwd_check(q, k, v, do, lists, mask, tag="", q_blocks=None, kv_blocks=None,
                o_dtype=torch.bfloat16):

@@ -51,9 +51,17 @@ def _mask_sampled(w, x, out, thr, heads):
 
 
 def _fwd_sampled(w, x, xg, lists, mask, nsamp, seed):
+    # The benchmark's configuration: the frame hint (paired query blocks); the
+    # unpaired kernel must give the same bits.
     nb = _nb()
-    o, lse = nb.nabla_sparse_attn_fwd(xg["q"], xg["k"], xg["v"], lists["kv_count"], lists["kv_idx"])
+    fb = (w.Hs // w.P) * (w.Ws // w.P)
+    o, lse = nb.nabla_sparse_attn_fwd(xg["q"], xg["k"], xg["v"], lists["kv_count"], lists["kv_idx"],
+                                      frame_blocks=fb)
+    o0, lse0 = nb.nabla_sparse_attn_fwd(xg["q"], xg["k"], xg["v"], lists["kv_count"], lists["kv_idx"])
     torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o0.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse0.view(torch.int32))
+    del o0, lse0
     rng = np.random.default_rng(seed)
     blocks = sorted(rng.choice(w.B * w.H * w.n, nsamp, replace=False).tolist())
     # Always include the longest and the shortest list.

@@ -535,8 +535,9 @@ def main() -> int:
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(step_flops),
             "algorithmic_flop_per_launch": step_flops,
-            "note": "forward call = per-head longest-first ordering kernel (one workgroup per head) + "
-                    "the attention kernel; events bracket both",
+            "note": "forward call = pair-count kernel + per-head longest-first ordering kernel + the "
+                    "attention kernel, events bracket all three; the kernel is limited by K/V traffic "
+                    "from beyond L2 (see traffic) and by its per-block step, not by the MFMA pipes",
         },
         "cpu_baseline": None,
     }

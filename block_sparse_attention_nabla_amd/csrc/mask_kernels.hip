@@ -286,6 +286,151 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The same selection with one wave per row, for rows of n <= 64 * VPL blocks:
+// the row stays in registers (lane l holds j = l + 64 r), every reduction is a
+// wave shuffle and the radix histograms live in a per-wave LDS slice, so no
+// workgroup barrier is needed. Four rows per 256-thread workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kSelWaveRows = 4;
+
+// Orders this wave's LDS accesses: the compiler may not move LDS operations
+// across it, and the wave waits until its own LDS operations have completed.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int MODE, int VPL>
+__global__ __launch_bounds__(256) void select_wave_kernel(
+    const float* __restrict__ logits, int64_t rows, int n, int keep_all, uint64_t bound,
+    StaParams sta, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_idx,
+    uint8_t* __restrict__ dense_mask, uint32_t* __restrict__ bits, int words_per_row) {
+    __shared__ unsigned long long hmass[kSelWaveRows][256];
+    __shared__ int hcnt[kSelWaveRows][256];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * kSelWaveRows + wave;
+    if (row >= rows) return;  // whole wave; no workgroup barrier follows
+    const int i = (int)(row % n);
+    float pv[VPL];
+    uint32_t tau = 0;
+    if (MODE != kSelSta) {
+        const float* L = logits + row * (int64_t)n;
+        // 1. row maximum; 2. exponentials and their sum; p = e / z
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) {
+            const int j = lane + 64 * r;
+            pv[r] = j < n ? L[j] : -INFINITY;
+            mx = fmaxf(mx, pv[r]);
+        }
+        mx = wave_max(mx);
+        float z = 0.f;
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) {
+            const int j = lane + 64 * r;
+            const float e = j < n ? expf(pv[r] - mx) : 0.f;
+            pv[r] = e;
+            z += e;
+        }
+        z = wave_sum(z);
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) pv[r] = pv[r] / z;
+
+        // 3. radix select of tau (see select_kernel): lane l owns bins 4l .. 4l+3.
+        if (!keep_all) {
+            unsigned long long* hm = hmass[wave];
+            int* hc = hcnt[wave];
+            uint32_t prefix = 0, pmask = 0;
+            unsigned long long above = 0;
+            for (int pass = 0; pass < 4; ++pass) {
+                const int shift = 24 - 8 * pass;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    hm[4 * lane + b] = 0ull;
+                    hc[4 * lane + b] = 0;
+                }
+                wave_lds_sync();
+#pragma unroll
+                for (int r = 0; r < VPL; ++r) {
+                    const int j = lane + 64 * r;
+                    const uint32_t key = __float_as_uint(pv[r]);
+                    if (j < n && (key & pmask) == prefix) {
+                        const int d = (key >> shift) & 255;
+                        const unsigned long long wgt =
+                            MODE == kSelTopk ? 1ull : (unsigned long long)__float2ull_rn(pv[r] * 0x1p40f);
+                        atomicAdd(&hm[d], wgt);
+                        atomicAdd(&hc[d], 1);
+                    }
+                }
+                wave_lds_sync();
+                unsigned long long m[4];
+                int cb[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    m[b] = hm[4 * lane + b];
+                    cb[b] = hc[4 * lane + b];
+                }
+                const unsigned long long local = (m[0] + m[1]) + (m[2] + m[3]);
+                unsigned long long incl = local;  // inclusive suffix sum over lanes
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const unsigned long long o = __shfl_down(incl, off);
+                    if (lane + off < 64) incl += o;
+                }
+                unsigned long long ab[4];  // weight strictly above each of this lane's bins
+                ab[3] = above + (incl - local);
+                ab[2] = ab[3] + m[3];
+                ab[1] = ab[2] + m[2];
+                ab[0] = ab[1] + m[1];
+                int cand = 256;
+#pragma unroll
+                for (int b = 3; b >= 0; --b)
+                    if (cb[b] > 0 && ab[b] <= bound) cand = 4 * lane + b;
+                int sel = cand;  // lowest qualifying bin of the wave
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) sel = min(sel, __shfl_xor(sel, off));
+                // < 256: the highest non-empty bin always qualifies.
+                unsigned long long mine = ab[0];
+#pragma unroll
+                for (int b = 1; b < 4; ++b)
+                    if ((sel & 3) == b) mine = ab[b];
+                above = __shfl(mine, sel >> 2);
+                prefix |= (uint32_t)sel << shift;
+                pmask |= 0xffu << shift;
+                wave_lds_sync();  // this pass's reads finish before the next pass clears
+            }
+            tau = prefix;
+        }
+    }
+
+    // 4. decisions, STA union, ascending compaction (chunk r = blocks 64r .. 64r+63)
+    int32_t* out_idx = kv_idx + row * (int64_t)n;
+    int running = 0;
+#pragma unroll
+    for (int r = 0; r < VPL; ++r) {
+        if (64 * r < n) {
+            const int j = lane + 64 * r;
+            bool keep = false;
+            if (j < n) {
+                if (MODE != kSelSta) keep = keep_all || __float_as_uint(pv[r]) >= tau;
+                if (!keep && sta.on) keep = sta_contains(sta, i, j);
+            }
+            const unsigned long long bal = __ballot(keep);
+            if (keep) out_idx[running + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+            if (dense_mask && j < n) dense_mask[row * (int64_t)n + j] = keep ? 1 : 0;
+            if (bits && lane < 2) {
+                const int word = 2 * r + lane;
+                if (word < words_per_row)
+                    bits[row * (int64_t)words_per_row + word] = (uint32_t)(bal >> (32 * lane));
+            }
+            running += __popcll(bal);
+        }
+    }
+    if (lane == 0) kv_count[row] = running;
+}
+
+// ---------------------------------------------------------------------------
 // Transpose of the kept-block relation: for key block j, the ascending list of
 // query blocks i that keep it. Workgroup = one 32-column word of the row
 // bitmasks; each wave owns 8 of those columns and walks the rows 64 at a time,
@@ -351,7 +496,28 @@ hipError_t launch_select(int mode, const float* logits, int64_t BH, int n, int k
                          uint64_t bound, const StaParams& sta, int32_t* kv_count, int32_t* kv_idx,
                          uint8_t* dense_mask, uint32_t* bits, int words_per_row,
                          hipStream_t stream) {
-    const unsigned grid = (unsigned)(BH * n);
+    const int64_t rows = BH * n;
+    // Content selectors on rows of up to 2048 blocks: one wave per row (values in
+    // registers). The STA window alone has no per-row reduction and runs faster
+    // with a workgroup per row.
+    if (n <= 2048 && mode != kSelSta) {
+        const unsigned wgrid = (unsigned)((rows + kSelWaveRows - 1) / kSelWaveRows);
+#define NABLA_SEL_WAVE(MODE_, VPL_)                                                             \
+    select_wave_kernel<MODE_, VPL_><<<wgrid, 64 * kSelWaveRows, 0, stream>>>(                   \
+        logits, rows, n, keep_all, bound, sta, kv_count, kv_idx, dense_mask, bits, words_per_row)
+#define NABLA_SEL_WAVE_MODES(VPL_)                                                              \
+    do {                                                                                        \
+        if (mode == kSelTopk) NABLA_SEL_WAVE(kSelTopk, VPL_);                                   \
+        else NABLA_SEL_WAVE(kSelCdf, VPL_);                                                     \
+    } while (0)
+        if (n <= 512) NABLA_SEL_WAVE_MODES(8);
+        else if (n <= 1024) NABLA_SEL_WAVE_MODES(16);
+        else NABLA_SEL_WAVE_MODES(32);
+#undef NABLA_SEL_WAVE_MODES
+#undef NABLA_SEL_WAVE
+        return hipGetLastError();
+    }
+    const unsigned grid = (unsigned)rows;
     if (mode == kSelTopk)
         select_kernel<kSelTopk><<<grid, kSelThreads, 0, stream>>>(
             logits, n, keep_all, bound, sta, kv_count, kv_idx, dense_mask, bits, words_per_row);

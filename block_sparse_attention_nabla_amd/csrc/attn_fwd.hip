@@ -80,24 +80,53 @@ __device__ __forceinline__ void load_rows(RowState<D>& st, const uint16_t* qrow_
 
 // One kept key block: K tile at kbase (lane base for the S^T A operand), V
 // tile at vbase (lane base for the transposing V^T reads).
-template <int D>
+// DEEP: read the K fragments further ahead of their products (all of tile 0,
+// then tile 1's reads interleaved with tile 0's MFMAs, the order pinned with
+// scheduling groups) -- 15 more registers; used where they fit 2 waves/SIMD.
+template <int D, bool DEEP>
 __device__ __forceinline__ void block_step(RowState<D>& st, const char* kbase, const char* vbase,
                                            float scale_log2) {
     using T = Tile<D>;
     constexpr int KK = RowState<D>::KK, DT = RowState<D>::DT;
     const uint32_t ones_bf16x2 = 0x3f803f80u;
 
-    // S^T (64 keys x 32 queries) as two 32 x 32 tiles; A fragments read first.
+    // S^T (64 keys x 32 queries) as two 32 x 32 tiles.
     f32x16_t s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        bf16x8_t a[KK];
+    if constexpr (DEEP) {
+        bf16x8_t a0[KK], a1[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-            a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + 32 * kt * T::KSTB + 32 * kk));
-        s[kt] = zero16();
+            a0[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + 32 * kk));
+        s[0] = zero16();
+        s[1] = zero16();
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s[kt] = mfma_32x32x16(a[kk], st.qf[kk], s[kt]);
+        for (int kk = 0; kk < KK; ++kk) {
+            a1[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + 32 * T::KSTB + 32 * kk));
+            s[0] = mfma_32x32x16(a0[kk], st.qf[kk], s[0]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s[1] = mfma_32x32x16(a1[kk], st.qf[kk], s[1]);
+        // Groups: KK LDS reads, then (1 MFMA, 1 LDS read) x KK, then KK MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, KK, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, KK, 0);
+    } else {
+        // A fragments of each tile read before its products (the compiler keeps
+        // about two reads in flight).
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            bf16x8_t a[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + 32 * kt * T::KSTB + 32 * kk));
+            s[kt] = zero16();
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) s[kt] = mfma_32x32x16(a[kk], st.qf[kk], s[kt]);
+        }
     }
 
     // Online softmax for query column c (keys split over this lane and lane ^ 32).
@@ -277,7 +306,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
         __syncthreads();
     }
     for (int it = 0; it < cnt; ++it) {
-        block_step<D>(st, kbase, vbase, scale_log2);
+        block_step<D, false>(st, kbase, vbase, scale_log2);
         if (it + 1 < cnt) {
             __syncthreads();  // every wave has read K_j and V_j
             NABLA_STAGE();  // block it+1, fetched one iteration ago
@@ -397,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
         __syncthreads();
         for (;;) {
             const int mine = grp ? (f_cur & 2) : (f_cur & 1);
-            if (mine && active) block_step<D>(st, kbase, vbase, scale_log2);
+            if (mine && active) block_step<D, true>(st, kbase, vbase, scale_log2);
             if (f_next == 0) break;  // the computed step was the last one
             __syncthreads();  // every wave is done with the staged tiles
             NABLA_PSTAGE();   // the step fetched one iteration ago

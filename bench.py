@@ -115,10 +115,22 @@ def summarize_traffic(fetch_csv: str, write_csv: str) -> dict:
     return res
 
 
-def cpu_baseline(w, x, thr: float, heads: int = 2) -> dict:
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, x, thr: float, heads: int = 2, gpu_dense_mask=None) -> dict:
     """The oracle on a bounded sample of the same workload: the whole hot path
     (mask, then the masked forward over every query block) for the first
-    `heads` heads; the rate is kept-block FLOP of the sample over its time."""
+    `heads` heads; the rate is kept-block FLOP of the sample over its time.
+    With the GPU's dense mask of those heads, also the mask parity counts
+    (blocks in the 1e-5 band of thr, mismatches, unexplained mismatches)."""
     import oracle
 
     q = x["q"].reshape(-1, w.S, w.D)[:heads].float()
@@ -132,8 +144,14 @@ def cpu_baseline(w, x, thr: float, heads: int = 2) -> dict:
     t_fwd = time.perf_counter() - t0
     kept = int(m["mask"].sum())
     flops = kept * 4.0 * w.N * w.N * w.D
+    parity = None
+    if gpu_dense_mask is not None:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from parity import compare_masks
+        parity = compare_masks(gpu_dense_mask[:heads], m, thr)
     return {"value": flops / (t_mask + t_fwd) / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu": cpu_model(), "kind": "oracle",
+            "mask_parity_sample": parity,
             "sample": (f"heads 0..{heads - 1} of {w.B * w.H}: mask ({t_mask:.1f} s) and forward over all "
                        f"{w.n} query blocks per head ({kept} kept blocks, {t_fwd:.1f} s); "
                        f"fp64 C + OpenMP"),
@@ -303,6 +321,15 @@ def train_step(args, dev, stream) -> dict:
     fwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
     fpk = 4.0 * w.N * w.N * D
+    # Mask sparsity at the calibrated thr on fresh Q/K sets (one seed per step).
+    del sets
+    per_step = []
+    for s_ in range(max(0, args.train_sparsity_steps)):
+        xs = synth.make_inputs(w, step=100 + s_, device=dev)
+        nb.nabla_build_mask(xs["q"], xs["k"], thr, out=lists, workspace=ws[nb.NABLA_OP_MASK],
+                            stream=stream)
+        per_step.append(round(1.0 - int(lists["kv_count"].sum()) / (B * H * n * n), 5))
+        del xs
     res = {
         "workload": f"{w.name}: {w.description}",
         "thr": round(thr, 6),
@@ -316,6 +343,7 @@ def train_step(args, dev, stream) -> dict:
         "step_tflops": round(3.5 * kept_last * fpk / (wall * 1e-3) / 1e12, 1),
         "flop_model": "forward 4*N*N*D, backward 10*N*N*D per kept block pair",
         "frame_blocks": fb,
+        "block_sparsity_per_fresh_step": per_step,
     }
     log(f"train: {res}")
     return res
@@ -337,6 +365,10 @@ def main() -> int:
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training-step figures (2B-DiT shape, forward + backward)")
     ap.add_argument("--train-steps", type=int, default=4)
+    ap.add_argument("--train-sparsity-steps", type=int, default=10,
+                    help="fresh Q/K sets whose mask sparsity is reported at the calibrated thr")
+    ap.add_argument("--cold-iters", type=int, default=5,
+                    help="mask + forward calls timed after a cache flush (0 = skip)")
     ap.add_argument("--no-pairs", action="store_true",
                     help="no frame hint: one query block per forward workgroup")
     ap.add_argument("--no-fidelity", action="store_true",
@@ -418,6 +450,13 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     mask_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    fwd_each = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    mask_each = sorted(e[0].elapsed_time(e[1]) for e in ev)
+
+    def pct(xs):
+        def at(f):
+            return xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
+        return {"p10": round(at(0.1), 4), "p50": round(at(0.5), 4), "p90": round(at(0.9), 4)}
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = step_flops / (fwd_ms * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms (mask {mask_ms:.3f} ms, forward {fwd_ms:.3f} ms); "
@@ -434,6 +473,26 @@ def main() -> int:
         torch.cuda.synchronize()
         unpaired_ms = e_u[0].elapsed_time(e_u[1]) / 5
         log(f"forward without the frame hint: {unpaired_ms:.3f} ms")
+
+    # Cold caches: a 512 MB write before each call evicts L2 and the Infinity Cache.
+    cold = None
+    if args.cold_iters > 0:
+        flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_iters)]
+        for i in range(args.cold_iters):
+            flush.fill_(i & 255)
+            ce[i][0].record(stream)
+            mask_step()
+            ce[i][1].record(stream)
+            flush.fill_((i + 1) & 255)
+            fwd_step()
+            ce[i][2].record(stream)
+        torch.cuda.synchronize()
+        cold = {"mask_ms": round(sum(e[0].elapsed_time(e[1]) for e in ce) / args.cold_iters, 4),
+                "forward_ms": round(sum(e[1].elapsed_time(e[2]) for e in ce) / args.cold_iters, 4),
+                "iters": args.cold_iters, "flush": "512 MB device write before each call"}
+        del flush
+        log(f"cold caches: {cold}")
 
     # Mask stage algorithmic bytes: read Q and K once, write counts and lists.
     mask_bytes = 2 * B * H * S * D * 2 + 4 * B * H * n + 4 * kept
@@ -518,6 +577,9 @@ def main() -> int:
         "forward_tflops": round(fwd_tflops, 2),
         "forward_ms": round(fwd_ms, 4),
         "forward_unpaired_ms": round(unpaired_ms, 4) if unpaired_ms is not None else None,
+        "forward_ms_percentiles": pct(fwd_each),
+        "mask_ms_percentiles": pct(mask_each),
+        "cold_caches": cold,
         "mask_ms": round(mask_ms, 4),
         "mask_gbps": round(mask_gbps, 1),
         "mask_pct_hbm_peak": round(100 * mask_gbps / PEAK_HBM_GBPS, 2),
@@ -558,7 +620,12 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         xc = {key: x[key] for key in ("q", "k", "v")}
-        result["cpu_baseline"] = cpu_baseline(w, xc, thr)
+        qh = xc["q"].reshape(-1, S, D)[:2].reshape(1, 2, S, D).to(dev)
+        kh = xc["k"].reshape(-1, S, D)[:2].reshape(1, 2, S, D).to(dev)
+        gm = nb.nabla_build_mask(qh, kh, thr, w.sta_struct(), dense=True)["dense_mask"]
+        gpu_dense = gm.reshape(2, n, n).cpu().numpy()
+        del qh, kh, gm
+        result["cpu_baseline"] = cpu_baseline(w, xc, thr, gpu_dense_mask=gpu_dense)
         log(f"cpu baseline {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
     return 0

@@ -392,13 +392,50 @@ __global__ __launch_bounds__(256) void select_wave_kernel(
                 for (int off = 32; off >= 1; off >>= 1) sel = min(sel, __shfl_xor(sel, off));
                 // < 256: the highest non-empty bin always qualifies.
                 unsigned long long mine = ab[0];
+                int cmine = cb[0];
 #pragma unroll
                 for (int b = 1; b < 4; ++b)
-                    if ((sel & 3) == b) mine = ab[b];
+                    if ((sel & 3) == b) {
+                        mine = ab[b];
+                        cmine = cb[b];
+                    }
                 above = __shfl(mine, sel >> 2);
+                const int csel = __shfl(cmine, sel >> 2);  // entries in the selected bin
                 prefix |= (uint32_t)sel << shift;
                 pmask |= 0xffu << shift;
-                wave_lds_sync();  // this pass's reads finish before the next pass clears
+                wave_lds_sync();  // this pass's reads finish before the LDS is reused
+                if (pass < 3 && csel <= 64) {
+                    // Few entries left: finish exactly. Each candidate's weight strictly
+                    // above is `above` plus the candidates with a larger bit pattern --
+                    // the same fixed-point sums the remaining passes would form, so tau
+                    // is the same. Candidates are compacted into LDS slots 0 .. csel-1.
+                    int base = 0;
+#pragma unroll
+                    for (int r = 0; r < VPL; ++r) {
+                        const int j = lane + 64 * r;
+                        const uint32_t key = __float_as_uint(pv[r]);
+                        const bool is_c = j < n && (key & pmask) == prefix;
+                        const unsigned long long bal = __ballot(is_c);
+                        if (is_c) {
+                            const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+                            hc[pos] = (int)key;
+                            hm[pos] = MODE == kSelTopk ? 1ull
+                                                       : (unsigned long long)__float2ull_rn(pv[r] * 0x1p40f);
+                        }
+                        base += __popcll(bal);
+                    }
+                    wave_lds_sync();
+                    const uint32_t my_key = lane < csel ? (uint32_t)hc[lane] : 0u;
+                    unsigned long long acc = 0;
+                    for (int m2 = 0; m2 < csel; ++m2)
+                        if ((uint32_t)hc[m2] > my_key) acc += hm[m2];
+                    uint32_t t = (lane < csel && above + acc <= bound) ? my_key : 0xffffffffu;
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1) t = min(t, (uint32_t)__shfl_xor((int)t, off));
+                    prefix = t;  // the largest candidate always qualifies
+                    wave_lds_sync();
+                    break;
+                }
             }
             tau = prefix;
         }

@@ -549,6 +549,7 @@ hipError_t launch_select(int mode, const float* logits, int64_t BH, int n, int k
     } while (0)
         if (n <= 512) NABLA_SEL_WAVE_MODES(8);
         else if (n <= 1024) NABLA_SEL_WAVE_MODES(16);
+        else if (n <= 1280) NABLA_SEL_WAVE_MODES(20);
         else NABLA_SEL_WAVE_MODES(32);
 #undef NABLA_SEL_WAVE_MODES
 #undef NABLA_SEL_WAVE

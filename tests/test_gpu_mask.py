@@ -106,10 +106,11 @@ def test_mask_ragged_shapes(B, H, n, D):
         _assert_parity(gpu, orc, thr)
 
 
-@pytest.mark.parametrize("n", [512, 513, 1024, 1025, 2048, 2049, 2100])
+@pytest.mark.parametrize("n", [512, 513, 1024, 1025, 1280, 1281, 2048, 2049, 2100])
 def test_mask_row_length_kernel_boundaries(n):
-    # Rows of up to 2048 blocks run one wave per row with 8, 16 or 32 values per
-    # lane; longer rows run one workgroup per row. Both sides of every boundary.
+    # Rows of up to 2048 blocks run one wave per row with 8, 16, 20 or 32 values per
+    # lane in registers; longer rows run one workgroup per row. Both sides of every
+    # boundary.
     q, k = _random_inputs(1, 1, 64 * n, 64, seed=n)
     for thr in (0.4,):
         gpu, orc = _run(q, k, thr)

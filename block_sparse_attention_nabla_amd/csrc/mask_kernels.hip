@@ -81,34 +81,61 @@ __global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ q
                                                      const float* __restrict__ ka,
                                                      float* __restrict__ logits, int n,
                                                      float scale) {
+    // Each wave computes a 64 x 64 tile as 2 x 2 MFMA tiles of 32 x 32, so every
+    // operand load feeds two products; the workgroup covers 128 x 128.
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = lane >> 5, c = lane & 31;
     const int64_t bh = blockIdx.z;
-    const int i0 = blockIdx.x * 64 + 32 * (wave >> 1);
-    const int j0 = blockIdx.y * 64 + 32 * (wave & 1);
+    const int i0 = blockIdx.x * 128 + 64 * (wave >> 1);
+    const int j0 = blockIdx.y * 128 + 64 * (wave & 1);
     if (i0 >= n || j0 >= n) return;  // whole-wave exit; no barriers below
-    const int qi = i0 + c, kj = j0 + c;
-    const float* qrow = qa + (bh * n + (qi < n ? qi : 0)) * D;
-    const float* krow = ka + (bh * n + (kj < n ? kj : 0)) * D;
-    const bool qok = qi < n, kok = kj < n;
-
-    f32x16_t acc = zero16();
-#pragma unroll 4
-    for (int d0 = 0; d0 < D; d0 += 8) {
-        float4 a = qok ? *reinterpret_cast<const float4*>(qrow + d0 + 4 * h) : make_float4(0, 0, 0, 0);
-        float4 b = kok ? *reinterpret_cast<const float4*>(krow + d0 + 4 * h) : make_float4(0, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
-    }
-    // C layout: this lane holds column j = j0 + c and rows i = i0 + c_row(r, h).
-    if (kok) {
+    const float* qrow[2];
+    const float* krow[2];
+    bool qok[2], kok[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = i0 + c_row(r, h);
-            if (i < n) logits[(bh * n + i) * (int64_t)n + kj] = acc[r] * scale;
+    for (int t = 0; t < 2; ++t) {
+        const int qi = i0 + 32 * t + c, kj = j0 + 32 * t + c;
+        qok[t] = qi < n;
+        kok[t] = kj < n;
+        qrow[t] = qa + (bh * n + (qok[t] ? qi : 0)) * D;
+        krow[t] = ka + (bh * n + (kok[t] ? kj : 0)) * D;
+    }
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int a_ = 0; a_ < 2; ++a_)
+#pragma unroll
+        for (int b_ = 0; b_ < 2; ++b_) acc[a_][b_] = zero16();
+#pragma unroll 2
+    for (int d0 = 0; d0 < D; d0 += 8) {
+        float4 a[2], b[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            a[t] = qok[t] ? *reinterpret_cast<const float4*>(qrow[t] + d0 + 4 * h) : make_float4(0, 0, 0, 0);
+            b[t] = kok[t] ? *reinterpret_cast<const float4*>(krow[t] + d0 + 4 * h) : make_float4(0, 0, 0, 0);
         }
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj) {
+                acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ti].x, b[tj].x, acc[ti][tj], 0, 0, 0);
+                acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ti].y, b[tj].y, acc[ti][tj], 0, 0, 0);
+                acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ti].z, b[tj].z, acc[ti][tj], 0, 0, 0);
+                acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ti].w, b[tj].w, acc[ti][tj], 0, 0, 0);
+            }
+    }
+    // C layout: this lane holds column j0 + 32 tj + c and rows i0 + 32 ti + c_row(r, h).
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) {
+        if (!kok[tj]) continue;
+        const int kj = j0 + 32 * tj + c;
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + 32 * ti + c_row(r, h);
+                if (i < n) logits[(bh * n + i) * (int64_t)n + kj] = acc[ti][tj][r] * scale;
+            }
     }
 }
 
@@ -521,7 +548,7 @@ hipError_t launch_pool(const void* q, const void* k, float* qa, float* ka, int64
 
 hipError_t launch_logits(const float* qa, const float* ka, float* logits, int64_t BH, int n, int D,
                          float scale, hipStream_t stream) {
-    dim3 grid((n + 63) / 64, (n + 63) / 64, (unsigned)BH);
+    dim3 grid((n + 127) / 128, (n + 127) / 128, (unsigned)BH);
     if (D == 128)
         logits_kernel<128><<<grid, 256, 0, stream>>>(qa, ka, logits, n, scale);
     else

@@ -150,6 +150,32 @@ def test_mask_exact_ties_are_kept_together():
         np.testing.assert_array_equal(dense[:, :8], dense[:, 8:])
 
 
+@pytest.mark.parametrize("groups", [(100, 200), (300,)])
+def test_mask_large_tie_groups(groups):
+    # Tie groups larger than a wave (64 entries share every bit of the probability):
+    # the selection cannot finish early and runs all four radix passes.
+    B, H, D = 1, 2, 64
+    n = sum(groups)
+    q, k = _random_inputs(B, H, 64 * n, D, seed=11)
+    k = k.reshape(B, H, n, 64, D)
+    start = 0
+    for g_i, size in enumerate(groups):
+        k[:, :, start:start + size] = k[:, :, start:start + 1].clone()
+        start += size
+    k = k.reshape(B, H, 64 * n, D).contiguous()
+    for thr in (0.3, 0.7, 0.99):
+        gpu, orc = _run(q, k, thr)
+        _assert_parity(gpu, orc, thr)
+        dense = gpu["dense_mask"].reshape(B * H, n, n)
+        start = 0
+        for size in groups:  # every group is kept or dropped whole
+            blk = dense[:, :, start:start + size]
+            assert (blk.min(axis=-1) == blk.max(axis=-1)).all()
+            start += size
+        if len(groups) == 1:
+            assert dense.all()  # one tie group: every entry has nothing strictly above it
+
+
 def test_mask_is_deterministic():
     nb = _nb()
     q, k = _random_inputs(1, 4, 64 * 150, 128, seed=6)

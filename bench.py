@@ -23,7 +23,9 @@ rocprofv3 with the counters FETCH_SIZE and WRITE_SIZE,
     python bench.py --summarize-traffic DIR/fetch_counter_collection.csv DIR/write_counter_collection.csv
 which scales each counter by what it reads for a plain 1 GiB copy kernel run
 in the same process and records the result, keyed to the forward kernel's
-source, for later bench runs.
+source, for later bench runs. With --traffic-kernel attn_fwd_kernel (counters
+taken with --no-pairs) it prints the one-block kernel's figures instead and
+records nothing.
 """
 
 from __future__ import annotations
@@ -74,8 +76,9 @@ def measured_traffic(launch_flops: float):
 CALIB_BYTES = 1 << 30  # copy-kernel calibration: read and write 1 GiB
 
 
-def summarize_traffic(fetch_csv: str, write_csv: str) -> dict:
-    """Per-launch HBM bytes of the forward kernel from two rocprofv3 counter CSVs."""
+def summarize_traffic(fetch_csv: str, write_csv: str, kernel: str = FWD_KERNEL) -> dict:
+    """Per-launch HBM bytes of a forward kernel from two rocprofv3 counter CSVs.
+    Only the figures of the kernel bench.py times (FWD_KERNEL) are recorded."""
     import csv
 
     def per_kernel(path, counter):
@@ -84,7 +87,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str) -> dict:
             if r["Counter_Name"] != counter:
                 continue
             kb = float(r["Counter_Value"])
-            if FWD_KERNEL in r["Kernel_Name"]:
+            if kernel + "<" in r["Kernel_Name"]:
                 out["fwd"].append(kb)
             elif "elementwise" in r["Kernel_Name"] and int(r["Grid_Size"]) > (1 << 20):
                 out["copy"].append(kb)
@@ -99,7 +102,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str) -> dict:
     fetch_b = sum(f["fwd"]) / len(f["fwd"]) * 1024.0 * f_scale
     write_b = sum(wr["fwd"]) / len(wr["fwd"]) * 1024.0 * w_scale
     res = {
-        "kernel": FWD_KERNEL,
+        "kernel": kernel,
         "workload": "wan14b_720p at 90% block sparsity",
         "fetch_bytes_per_launch": fetch_b,
         "write_bytes_per_launch": write_b,
@@ -109,6 +112,8 @@ def summarize_traffic(fetch_csv: str, write_csv: str) -> dict:
         "launches": {"fetch": len(f["fwd"]), "write": len(wr["fwd"])},
         "kernel_source_sha256_16": source_hash(FWD_SOURCE),
     }
+    if kernel != FWD_KERNEL:
+        return res
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(res, fh, indent=2)
@@ -362,6 +367,8 @@ def main() -> int:
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="also run a plain 1 GiB copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--traffic-kernel", default=FWD_KERNEL,
+                    help="kernel whose counters --summarize-traffic reads (attn_fwd_kernel: print only)")
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training-step figures (2B-DiT shape, forward + backward)")
     ap.add_argument("--train-steps", type=int, default=4)
@@ -380,7 +387,7 @@ def main() -> int:
     ap.add_argument("--reorder-iters", type=int, default=10)
     args = ap.parse_args()
     if args.summarize_traffic:
-        print(json.dumps(summarize_traffic(*args.summarize_traffic)))
+        print(json.dumps(summarize_traffic(*args.summarize_traffic, kernel=args.traffic_kernel)))
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "

@@ -14,7 +14,8 @@
 //   the accumulator's slot map, so neither P nor V is ever shuffled.
 // K and V tiles are prefetched two blocks ahead into registers with plain
 // 16-byte loads and written to padded LDS rows after the current block's
-// reads, so global latency overlaps a whole block of compute. exp2 is used
+// reads (the pair kernel below double-buffers them), so global latency
+// overlaps a whole block of compute. exp2 is used
 // with log2(e) folded into the scale, and the output is rescaled only when a
 // row maximum grows by more than 2^8. A wave raises its issue priority for the
 // duration of a block step: a SIMD holds two waves, and one that is computing
@@ -343,6 +344,9 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
 // union steps ahead for the prefetch. Each union step carries two flags (in
 // A's list, in B's list); a pair of waves computes a step only if its flag is
 // set, so each block sees exactly its own kept blocks in ascending order.
+// The K/V tiles are double-buffered in LDS (75.8 KB at D = 128; two workgroups
+// still fit a CU): a wave stages the next step into the other buffer right
+// after computing the current one, and one barrier per step suffices.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -351,8 +355,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
     float scale_log2, void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
     using T = Tile<D>;
     constexpr int L = T::CHUNKS / 256;  // 16-byte chunks per thread per tile
-    __shared__ __attribute__((aligned(16))) char sK[kBlockN * T::KSTB];
-    __shared__ __attribute__((aligned(16))) char sV[kBlockN * T::VSTB];
+    constexpr int KB = kBlockN * T::KSTB, VB = kBlockN * T::VSTB;
+    __shared__ __attribute__((aligned(16))) char sK[2 * KB];
+    __shared__ __attribute__((aligned(16))) char sV[2 * VB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -414,13 +419,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
             vr[i_] = *reinterpret_cast<const u32x4_t*>(vh + off_ + e_ * 8);    \
         }                                                                      \
     } while (0)
-#define NABLA_PSTAGE()                                                         \
+#define NABLA_PSTAGE(B)                                                        \
     do {                                                                       \
         _Pragma("unroll") for (int i_ = 0; i_ < L; ++i_) {                     \
             const int e_ = tid + 256 * i_;                                     \
             const int r_ = e_ / T::CPR, ch_ = e_ % T::CPR;                     \
-            *reinterpret_cast<u32x4_t*>(sK + r_ * T::KSTB + 16 * ch_) = kr[i_];\
-            *reinterpret_cast<u32x4_t*>(sV + r_ * T::VSTB + 16 * ch_) = vr[i_];\
+            char* kd_ = sK + (B) * KB + r_ * T::KSTB + 16 * ch_;                 \
+            char* vd_ = sV + (B) * VB + r_ * T::VSTB + 16 * ch_;                 \
+            *reinterpret_cast<u32x4_t*>(kd_) = kr[i_];                         \
+            *reinterpret_cast<u32x4_t*>(vd_) = vr[i_];                         \
         }                                                                      \
     } while (0)
 
@@ -432,9 +439,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
     int f_cur = 0, f_next = 0;  // flags of the staged step and of the step in flight
     int j_tmp;
     if (cntA + cntB > 0) {
+        int buf = 0;
         step(pre, j_tmp, f_cur);
         NABLA_PFETCH(j_tmp);
-        NABLA_PSTAGE();
+        NABLA_PSTAGE(0);
         if (pre.ia < cntA || pre.ib < cntB) {
             step(pre, j_tmp, f_next);
             NABLA_PFETCH(j_tmp);
@@ -442,10 +450,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
         __syncthreads();
         for (;;) {
             const int mine = grp ? (f_cur & 2) : (f_cur & 1);
-            if (mine && active) block_step<D, true>(st, kbase, vbase, scale_log2);
+            if (mine && active) block_step<D, true>(st, kbase + buf * KB, vbase + buf * VB, scale_log2);
             if (f_next == 0) break;  // the computed step was the last one
-            __syncthreads();  // every wave is done with the staged tiles
-            NABLA_PSTAGE();   // the step fetched one iteration ago
+            // The other buffer's readers finished before the last barrier.
+            NABLA_PSTAGE(buf ^ 1);  // the step fetched one iteration ago
             f_cur = f_next;
             f_next = 0;
             if (pre.ia < cntA || pre.ib < cntB) {
@@ -453,6 +461,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
                 NABLA_PFETCH(j_tmp);
             }
             __syncthreads();
+            buf ^= 1;
         }
     }
 

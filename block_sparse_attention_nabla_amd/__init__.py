@@ -16,11 +16,17 @@ Entry points (same names as the C ABI):
     nabla_block_mass(q, k, lse)                      -> dense block masses [B,H,n,n]
     nabla_mask_recall(mass, kv_count, kv_idx)        -> (recall, best_recall) per row
     nabla_workspace_size(op, B, H, S, D, N), nabla_status_string(code)
+
+Streams: every entry point launches on ``stream`` (a torch.cuda.Stream), else on
+the current stream. With an explicit stream, the tensors a call allocates
+(outputs, workspace) are allocated on that stream too, so the caching allocator
+never hands them to other work while the call's kernels may still use them.
 """
 
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 from typing import Dict, Optional, Tuple
@@ -127,6 +133,20 @@ def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run an entry point with ``stream`` (when given) as the current stream, so
+    that its allocations belong to the stream its kernels run on."""
+
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kwargs)
+
+    return wrapper
+
+
 def _check_qkv(name: str, t: torch.Tensor, shape=None):
     if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
         raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, S, D]")
@@ -180,6 +200,7 @@ def _content_mask(fn_name, q, k, select_arg, sta, N, transpose, dense, out, work
     return res
 
 
+@_on_stream
 def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, sta: Optional[dict] = None,
                      N: int = BLOCK_N, *, transpose: bool = False, dense: bool = False,
                      out: Optional[Dict[str, torch.Tensor]] = None,
@@ -194,6 +215,7 @@ def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, sta: Optional
                          workspace, stream)
 
 
+@_on_stream
 def nabla_build_topk_mask(q: torch.Tensor, k: torch.Tensor, topk: int, sta: Optional[dict] = None,
                           N: int = BLOCK_N, *, transpose: bool = False, dense: bool = False,
                           out: Optional[Dict[str, torch.Tensor]] = None,
@@ -205,6 +227,7 @@ def nabla_build_topk_mask(q: torch.Tensor, k: torch.Tensor, topk: int, sta: Opti
                          workspace, stream)
 
 
+@_on_stream
 def nabla_build_sta_mask(B: int, H: int, S: int, sta: dict, device, N: int = BLOCK_N, *,
                          transpose: bool = False, dense: bool = False,
                          out: Optional[Dict[str, torch.Tensor]] = None,
@@ -229,6 +252,7 @@ def nabla_build_sta_mask(B: int, H: int, S: int, sta: dict, device, N: int = BLO
     return res
 
 
+@_on_stream
 def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           kv_count: torch.Tensor, kv_idx: torch.Tensor,
                           softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
@@ -271,6 +295,7 @@ def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return o, (lse if want_lse else None)
 
 
+@_on_stream
 def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx,
                           softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
                           dq=None, dk=None, dv=None, workspace=None,
@@ -307,6 +332,7 @@ def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx
     return dq, dk, dv
 
 
+@_on_stream
 def nabla_block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor,
                      softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -332,6 +358,7 @@ def nabla_block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor,
     return out
 
 
+@_on_stream
 def nabla_mask_recall(mass: torch.Tensor, kv_count: torch.Tensor, kv_idx: torch.Tensor,
                       N: int = BLOCK_N, *, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per row: block mass inside the kept lists, and inside the best blocks at the same count."""
@@ -350,6 +377,7 @@ def nabla_mask_recall(mass: torch.Tensor, kv_count: torch.Tensor, kv_idx: torch.
     return recall, best
 
 
+@_on_stream
 def nabla_reorder_tokens(x: torch.Tensor, T: int, Hs: int, Ws: int, P: int, inverse: bool = False,
                          *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Token reordering of section 3.1.1 (Figure 3) or its inverse, out of place.

@@ -605,8 +605,10 @@ def main() -> int:
             "traffic": measured_traffic(step_flops),
             "algorithmic_flop_per_launch": step_flops,
             "note": "forward call = pair-count kernel + per-head longest-first ordering kernel + the "
-                    "attention kernel, events bracket all three; the kernel is limited by K/V traffic "
-                    "from beyond L2 (see traffic) and by its per-block step, not by the MFMA pipes",
+                    "attention kernel, events bracket all three; the kernel is limited by its "
+                    "per-block step (softmax VALU and MFMA from one wave) and by keeping its four "
+                    "waves in step, not by the MFMA pipes; its traffic beyond L2 (see traffic) moves "
+                    "at ~5 TB/s, below the ~7 TB/s the one-block kernel sustains",
         },
         "cpu_baseline": None,
         "context": {

@@ -317,8 +317,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 // the row stays in registers (lane l holds j = l + 64 r), every reduction is a
 // wave shuffle and the radix histograms live in a per-wave LDS slice, so no
 // workgroup barrier is needed. Four rows per 256-thread workgroup.
+// A histogram bin is one 64-bit word, (weight << kCntBits) + count, so each
+// entry costs one LDS atomic; the fields cannot carry into each other (counts
+// <= NABLA_MAX_BLOCKS < 2^kCntBits, weights sum to < 2^41). Each wave keeps
+// kSelCopies copies of its histogram, lane l adding into copy l % kSelCopies:
+// neighbouring key blocks tend to share a bin, and the copies spread those
+// same-address atomics over different words.
 // ---------------------------------------------------------------------------
 constexpr int kSelWaveRows = 4;
+constexpr int kSelCopies = 4;
+constexpr int kCntBits = 14;
+static_assert(NABLA_MAX_BLOCKS < (1 << kCntBits), "bin counts must fit their field");
 
 // Orders this wave's LDS accesses: the compiler may not move LDS operations
 // across it, and the wave waits until its own LDS operations have completed.
@@ -332,8 +341,7 @@ __global__ __launch_bounds__(256) void select_wave_kernel(
     const float* __restrict__ logits, int64_t rows, int n, int keep_all, uint64_t bound,
     StaParams sta, int32_t* __restrict__ kv_count, int32_t* __restrict__ kv_idx,
     uint8_t* __restrict__ dense_mask, uint32_t* __restrict__ bits, int words_per_row) {
-    __shared__ unsigned long long hmass[kSelWaveRows][256];
-    __shared__ int hcnt[kSelWaveRows][256];
+    __shared__ __attribute__((aligned(16))) unsigned long long hist[kSelWaveRows][kSelCopies][256];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t row = (int64_t)blockIdx.x * kSelWaveRows + wave;
@@ -366,17 +374,20 @@ __global__ __launch_bounds__(256) void select_wave_kernel(
 
         // 3. radix select of tau (see select_kernel): lane l owns bins 4l .. 4l+3.
         if (!keep_all) {
-            unsigned long long* hm = hmass[wave];
-            int* hc = hcnt[wave];
+            unsigned long long(*hw)[256] = hist[wave];
+            unsigned long long* mine_copy = hw[lane % kSelCopies];
             uint32_t prefix = 0, pmask = 0;
             unsigned long long above = 0;
             for (int pass = 0; pass < 4; ++pass) {
                 const int shift = 24 - 8 * pass;
+                // The weights are recomputed each pass rather than kept live across
+                // passes (VPL 64-bit registers): the scale is made opaque per pass.
+                float two40 = 0x1p40f;
+                asm volatile("" : "+s"(two40));
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    hm[4 * lane + b] = 0ull;
-                    hc[4 * lane + b] = 0;
-                }
+                for (int cp = 0; cp < kSelCopies; ++cp)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) hw[cp][4 * lane + b] = 0ull;
                 wave_lds_sync();
 #pragma unroll
                 for (int r = 0; r < VPL; ++r) {
@@ -385,9 +396,8 @@ __global__ __launch_bounds__(256) void select_wave_kernel(
                     if (j < n && (key & pmask) == prefix) {
                         const int d = (key >> shift) & 255;
                         const unsigned long long wgt =
-                            MODE == kSelTopk ? 1ull : (unsigned long long)__float2ull_rn(pv[r] * 0x1p40f);
-                        atomicAdd(&hm[d], wgt);
-                        atomicAdd(&hc[d], 1);
+                            MODE == kSelTopk ? 1ull : (unsigned long long)__float2ull_rn(pv[r] * two40);
+                        atomicAdd(&mine_copy[d], (wgt << kCntBits) + 1ull);
                     }
                 }
                 wave_lds_sync();
@@ -395,8 +405,11 @@ __global__ __launch_bounds__(256) void select_wave_kernel(
                 int cb[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    m[b] = hm[4 * lane + b];
-                    cb[b] = hc[4 * lane + b];
+                    unsigned long long packed = 0;
+#pragma unroll
+                    for (int cp = 0; cp < kSelCopies; ++cp) packed += hw[cp][4 * lane + b];
+                    m[b] = packed >> kCntBits;
+                    cb[b] = (int)(packed & ((1ull << kCntBits) - 1ull));
                 }
                 const unsigned long long local = (m[0] + m[1]) + (m[2] + m[3]);
                 unsigned long long incl = local;  // inclusive suffix sum over lanes
@@ -435,7 +448,10 @@ __global__ __launch_bounds__(256) void select_wave_kernel(
                     // Few entries left: finish exactly. Each candidate's weight strictly
                     // above is `above` plus the candidates with a larger bit pattern --
                     // the same fixed-point sums the remaining passes would form, so tau
-                    // is the same. Candidates are compacted into LDS slots 0 .. csel-1.
+                    // is the same. Candidates are compacted into LDS slots 0 .. csel-1
+                    // (keys in histogram copy 1 read as 32-bit words, weights in copy 0).
+                    uint32_t* hc = reinterpret_cast<uint32_t*>(hw[1]);
+                    unsigned long long* hm = hw[0];
                     int base = 0;
 #pragma unroll
                     for (int r = 0; r < VPL; ++r) {
@@ -445,17 +461,17 @@ __global__ __launch_bounds__(256) void select_wave_kernel(
                         const unsigned long long bal = __ballot(is_c);
                         if (is_c) {
                             const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-                            hc[pos] = (int)key;
+                            hc[pos] = key;
                             hm[pos] = MODE == kSelTopk ? 1ull
                                                        : (unsigned long long)__float2ull_rn(pv[r] * 0x1p40f);
                         }
                         base += __popcll(bal);
                     }
                     wave_lds_sync();
-                    const uint32_t my_key = lane < csel ? (uint32_t)hc[lane] : 0u;
+                    const uint32_t my_key = lane < csel ? hc[lane] : 0u;
                     unsigned long long acc = 0;
                     for (int m2 = 0; m2 < csel; ++m2)
-                        if ((uint32_t)hc[m2] > my_key) acc += hm[m2];
+                        if (hc[m2] > my_key) acc += hm[m2];
                     uint32_t t = (lane < csel && above + acc <= bound) ? my_key : 0xffffffffu;
 #pragma unroll
                     for (int off = 32; off >= 1; off >>= 1) t = min(t, (uint32_t)__shfl_xor((int)t, off));

@@ -106,13 +106,24 @@ __global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ q
     for (int a_ = 0; a_ < 2; ++a_)
 #pragma unroll
         for (int b_ = 0; b_ < 2; ++b_) acc[a_][b_] = zero16();
+    // The next step's operands are loaded before this step's products.
+    float4 na[2], nb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        na[t] = qok[t] ? *reinterpret_cast<const float4*>(qrow[t] + 4 * h) : make_float4(0, 0, 0, 0);
+        nb[t] = kok[t] ? *reinterpret_cast<const float4*>(krow[t] + 4 * h) : make_float4(0, 0, 0, 0);
+    }
 #pragma unroll 2
     for (int d0 = 0; d0 < D; d0 += 8) {
         float4 a[2], b[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            a[t] = qok[t] ? *reinterpret_cast<const float4*>(qrow[t] + d0 + 4 * h) : make_float4(0, 0, 0, 0);
-            b[t] = kok[t] ? *reinterpret_cast<const float4*>(krow[t] + d0 + 4 * h) : make_float4(0, 0, 0, 0);
+            a[t] = na[t];
+            b[t] = nb[t];
+            if (d0 + 8 < D) {
+                na[t] = qok[t] ? *reinterpret_cast<const float4*>(qrow[t] + d0 + 8 + 4 * h) : make_float4(0, 0, 0, 0);
+                nb[t] = kok[t] ? *reinterpret_cast<const float4*>(krow[t] + d0 + 8 + 4 * h) : make_float4(0, 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)

@@ -42,10 +42,12 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
 
     const int t = threadIdx.x;
     const int cg = t % CG, r0 = t / CG;
+    // Every Q/K byte is read once here: non-temporal loads stream past the caches.
     uint4 raw[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
-        raw[p] = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + p * RPT) * D + cg * 8);
+        raw[p] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                                               src + (int64_t)(r0 + p * RPT) * D + cg * 8)));
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;

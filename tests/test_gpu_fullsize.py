@@ -112,8 +112,9 @@ def test_dit2b_train_mask_forward_backward():
                                           out["kv_idx"], out["q_count"], out["q_idx"])
     torch.cuda.synchronize()
     rng = np.random.default_rng(6)
-    qb = sorted(rng.choice(w.B * w.H * w.n, 4, replace=False).tolist())
-    kb = sorted(rng.choice(w.B * w.H * w.n, 3, replace=False).tolist())
+    # Two query blocks (dQ) and two key blocks (dK, dV) sampled in every head.
+    qb = sorted(bh * w.n + int(i) for bh in range(w.B * w.H) for i in rng.choice(w.n, 2, replace=False))
+    kb = sorted(bh * w.n + int(i) for bh in range(w.B * w.H) for i in rng.choice(w.n, 2, replace=False))
     rdq, rdk, rdv = oracle.attn_bwd(x["q"].float(), x["k"].float(), x["v"].float(), x["do"].float(), mask,
                                     w.N, q_blocks=qb, kv_blocks=kb)
     res = {}

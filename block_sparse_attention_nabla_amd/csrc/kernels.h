@@ -16,17 +16,43 @@ struct StaParams {
     int wt, wh, ww;
 };
 
-hipError_t launch_pool(const void* q, const void* k, float* qa, float* ka, int64_t nblocks, int D,
+// Outputs of the pooling stage (all [BH, n, ...] in block order).
+struct PoolOut {
+    float* qa;      // fp32 block means of Q [BH, n, D] (operands of the reduced logits)
+    float* ka;      // fp32 block means of K
+    double* qa64;   // the exact block means in fp64 [BH, n, D]
+    double* ka64;
+    float* qnorm;   // |Q_a[i]|_2, rounded up [BH, n]
+    float* knorm;   // |K_a[j]|_2, rounded up [BH, n]
+    float* kmax;    // max_j |K_a[j]|_2 per head [BH]
+};
+hipError_t launch_pool(const void* q, const void* k, const PoolOut& out, int64_t BH, int n, int D,
                        hipStream_t stream);
 hipError_t launch_logits(const float* qa, const float* ka, float* logits, int64_t BH, int n, int D,
                          float scale, hipStream_t stream);
 // Row selectors of launch_select. bound: kSelCdf -> floor(thr * 2^40) (fixed-point
-// mass); kSelTopk -> k - 1 (a count); kSelSta -> unused (logits may be null).
+// mass); kSelTopk -> k - 1 (a count); kSelSta -> unused (no logits needed).
 enum { kSelCdf = 0, kSelTopk = 1, kSelSta = 2 };
-hipError_t launch_select(int mode, const float* logits, int64_t BH, int n, int keep_all,
-                         uint64_t bound, const StaParams& sta, int32_t* kv_count, int32_t* kv_idx,
-                         uint8_t* dense_mask, uint32_t* bits, int words_per_row,
-                         hipStream_t stream);
+struct SelectArgs {
+    const float* logits;   // fp32 reduced logits [rows, n] (unused by kSelSta)
+    int64_t rows;          // BH * n
+    int n;
+    int keep_all;
+    uint64_t bound;
+    StaParams sta;
+    const double* qa64;    // exact block means (PoolOut)
+    const double* ka64;
+    const float* qnorm;
+    const float* kmax;
+    double scale64;        // softmax scale in fp64 (1/sqrt(D))
+    float err_unit;        // fp32 logit error bound per unit |Q_a| |K_a| (see select_wave_kernel)
+    int32_t* kv_count;
+    int32_t* kv_idx;
+    uint8_t* dense_mask;
+    uint32_t* bits;
+    int words_per_row;
+};
+hipError_t launch_select(int mode, const SelectArgs& args, int D, hipStream_t stream);
 hipError_t launch_transpose(const uint32_t* bits, int64_t BH, int n, int words_per_row,
                             int32_t* q_count, int32_t* q_idx, hipStream_t stream);
 

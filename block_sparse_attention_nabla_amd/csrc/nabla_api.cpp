@@ -20,6 +20,17 @@ inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; 
         if ((expr) != hipSuccess) return NABLA_ERR_HIP; \
     } while (0)
 
+// Bound on |L' - L| per unit of |Q_a[i]|_2 |K_a[j]|_2 for the fp32 reduced logit
+// L' = fl(fl(sum_d fl(qa_d) fl(ka_d)) * fl(1/sqrt(D))) against the exact
+// L = (1/sqrt(D)) sum_d qa_d ka_d: the D-term fp32 dot product contributes
+// gamma_(D+2) = (D+2)u/(1-(D+2)u) of sum_d |qa_d ka_d| <= |qa| |ka| (products
+// possibly rounded too), the fp32 operands 2u, the fp32 scale and the final
+// multiply 2u each -- (D + 8) u in all, u = 2^-24, with a 1% margin.
+float logit_error_unit(int D, float scale) {
+    const double u = 1.0 / 16777216.0;
+    return (float)((D + 8) * u * 1.01 * (double)scale * (1.0 + 1e-6));
+}
+
 StaParams sta_params(const nabla_sta_t* sta) {
     StaParams sp{};
     if (sta) {
@@ -52,18 +63,40 @@ nabla_status_t content_mask(int mode, int keep_all, uint64_t bound, const void* 
     const MaskWorkspace w = mask_workspace(s);
     if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
 
-    const StaParams sp = sta_params(sta);
-    float* qa = reinterpret_cast<float*>(ws_at(workspace, w.qa));
-    float* ka = reinterpret_cast<float*>(ws_at(workspace, w.ka));
+    PoolOut po;
+    po.qa = reinterpret_cast<float*>(ws_at(workspace, w.qa));
+    po.ka = reinterpret_cast<float*>(ws_at(workspace, w.ka));
+    po.qa64 = reinterpret_cast<double*>(ws_at(workspace, w.qa64));
+    po.ka64 = reinterpret_cast<double*>(ws_at(workspace, w.ka64));
+    po.qnorm = reinterpret_cast<float*>(ws_at(workspace, w.qnorm));
+    po.knorm = reinterpret_cast<float*>(ws_at(workspace, w.knorm));
+    po.kmax = reinterpret_cast<float*>(ws_at(workspace, w.kmax));
     float* logits = reinterpret_cast<float*>(ws_at(workspace, w.logits));
     uint32_t* bits = q_idx ? reinterpret_cast<uint32_t*>(ws_at(workspace, w.bits)) : nullptr;
     hipStream_t hs = as_stream(stream);
 
-    NABLA_LAUNCH(launch_pool(q, k, qa, ka, s.BH * s.n, (int)s.D, hs));
-    NABLA_LAUNCH(launch_logits(qa, ka, logits, s.BH, (int)s.n, (int)s.D,
-                               1.0f / sqrtf((float)s.D), hs));
-    NABLA_LAUNCH(launch_select(mode, logits, s.BH, (int)s.n, keep_all, bound, sp, kv_count, kv_idx,
-                               dense_mask, bits, w.words_per_row, hs));
+    const float scale = 1.0f / sqrtf((float)s.D);
+    NABLA_LAUNCH(launch_pool(q, k, po, s.BH, (int)s.n, (int)s.D, hs));
+    NABLA_LAUNCH(launch_logits(po.qa, po.ka, logits, s.BH, (int)s.n, (int)s.D, scale, hs));
+    SelectArgs a{};
+    a.logits = logits;
+    a.rows = s.BH * s.n;
+    a.n = (int)s.n;
+    a.keep_all = keep_all;
+    a.bound = bound;
+    a.sta = sta_params(sta);
+    a.qa64 = po.qa64;
+    a.ka64 = po.ka64;
+    a.qnorm = po.qnorm;
+    a.kmax = po.kmax;
+    a.scale64 = 1.0 / sqrt((double)s.D);
+    a.err_unit = logit_error_unit((int)s.D, scale);
+    a.kv_count = kv_count;
+    a.kv_idx = kv_idx;
+    a.dense_mask = dense_mask;
+    a.bits = bits;
+    a.words_per_row = w.words_per_row;
+    NABLA_LAUNCH(launch_select(mode, a, (int)s.D, hs));
     if (q_idx)
         NABLA_LAUNCH(launch_transpose(bits, s.BH, (int)s.n, w.words_per_row, q_count, q_idx, hs));
     return NABLA_OK;
@@ -136,8 +169,16 @@ nabla_status_t nabla_build_sta_mask(int32_t B, int32_t H, int32_t S, int32_t N,
 
     uint32_t* bits = q_idx ? reinterpret_cast<uint32_t*>(ws_at(workspace, w.bits)) : nullptr;
     hipStream_t hs = as_stream(stream);
-    NABLA_LAUNCH(launch_select(kSelSta, nullptr, s.BH, (int)s.n, 0, 0, sta_params(sta), kv_count,
-                               kv_idx, dense_mask, bits, w.words_per_row, hs));
+    SelectArgs a{};
+    a.rows = s.BH * s.n;
+    a.n = (int)s.n;
+    a.sta = sta_params(sta);
+    a.kv_count = kv_count;
+    a.kv_idx = kv_idx;
+    a.dense_mask = dense_mask;
+    a.bits = bits;
+    a.words_per_row = w.words_per_row;
+    NABLA_LAUNCH(launch_select(kSelSta, a, (int)s.D, hs));
     if (q_idx)
         NABLA_LAUNCH(launch_transpose(bits, s.BH, (int)s.n, w.words_per_row, q_count, q_idx, hs));
     return NABLA_OK;

@@ -38,9 +38,15 @@ MaskWorkspace mask_workspace(const Shape& s) {
     MaskWorkspace w;
     const size_t pooled = (size_t)s.BH * s.n * s.D * sizeof(float);
     w.words_per_row = (int)((s.n + 31) / 32);
+    const size_t norms = (size_t)s.BH * s.n * sizeof(float);
     w.qa = 0;
     w.ka = w.qa + align256(pooled);
-    w.logits = w.ka + align256(pooled);
+    w.qa64 = w.ka + align256(pooled);
+    w.ka64 = w.qa64 + align256(2 * pooled);
+    w.qnorm = w.ka64 + align256(2 * pooled);
+    w.knorm = w.qnorm + align256(norms);
+    w.kmax = w.knorm + align256(norms);
+    w.logits = w.kmax + align256((size_t)s.BH * sizeof(float));
     w.bits = w.logits + align256((size_t)s.BH * s.n * s.n * sizeof(float));
     w.total = w.bits + align256((size_t)s.BH * s.n * w.words_per_row * sizeof(uint32_t));
     return w;

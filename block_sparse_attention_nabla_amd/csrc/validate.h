@@ -15,7 +15,7 @@ struct Shape {
 
 // Region offsets inside a caller-provided workspace (all 256-byte aligned).
 struct MaskWorkspace {
-    size_t qa, ka, logits, bits, total;
+    size_t qa, ka, qa64, ka64, qnorm, knorm, kmax, logits, bits, total;
     int words_per_row;
 };
 struct StaWorkspace {

@@ -109,7 +109,7 @@ def test_mask_ragged_shapes(B, H, n, D):
 @pytest.mark.parametrize("n", [512, 513, 1024, 1025, 1280, 1281, 2048, 2049, 2100])
 def test_mask_row_length_kernel_boundaries(n):
     # Rows of up to 2048 blocks run one wave per row with 8, 16, 20 or 32 values per
-    # lane in registers; longer rows run one workgroup per row. Both sides of every
+    # lane in registers; longer rows keep the row in LDS. Both sides of every
     # boundary.
     q, k = _random_inputs(1, 1, 64 * n, 64, seed=n)
     for thr in (0.4,):
@@ -197,3 +197,67 @@ def test_mask_row_constant_key_shift_invariance():
     g2, orc2 = _run(q, k2, 0.5)
     r1 = compare_masks(g2["dense_mask"].reshape(orc1["mask"].shape), orc2, 0.5)
     assert r1["unexplained"] == 0, r1
+
+
+def _near_tied_pair(seed=21, n=32, D=64, b=9):
+    """Key block b = key block a (a = row 0's second-largest block) with one bf16
+    element nudged by one unit in the last place (the smallest element of the
+    feature where row 0's pooled query is smallest): the two reduced probabilities of row 0 differ by
+    ~1e-8 relative, below what fp32 logits resolve. Returns bf16 q, k, the
+    oracle's fp64 reduced map and a."""
+    g = torch.Generator().manual_seed(seed)
+    base = torch.randn((1, 1, n, 1, D), generator=g)
+    q = (torch.randn((1, 1, n, 64, D), generator=g) + base).reshape(1, 1, 64 * n, D).bfloat16()
+    k = (torch.randn((1, 1, n, 64, D), generator=g) + base).reshape(1, 1, n, 64, D).bfloat16()
+    qa = oracle.pool(q.float(), 64)[0]
+    p0 = oracle.reduced_map(qa[None], oracle.pool(k.reshape(1, 1, 64 * n, D).float(), 64),
+                            1.0 / np.sqrt(D))[0]
+    a = int(np.argsort(-p0[0])[1])
+    assert a != b
+    k[:, :, b] = k[:, :, a]
+    d = int(np.argmin(np.abs(qa[0])))
+    col = k[0, 0, b, :, d].float().abs()
+    r = int(torch.argmin(torch.where(col > 0, col, torch.full_like(col, 1e30))))  # smallest ulp
+    bits = k[0, 0, b, r, d].view(torch.int16).item()
+    k[0, 0, b, r, d] = torch.tensor([bits + 1], dtype=torch.int16).view(torch.bfloat16)[0]
+    k = k.reshape(1, 1, 64 * n, D).contiguous()
+    p = oracle.reduced_map(qa[None], oracle.pool(k.float(), 64), 1.0 / np.sqrt(D))[0]
+    return q, k, p, a
+
+
+def test_mask_order_below_fp32_resolution_is_exact():
+    # Two probabilities closer than fp32 rounding, with thr placed between their
+    # mass-above values (half the larger probability away from each, far outside
+    # the 1e-5 band): only the larger one may be kept, as in the oracle.
+    b = 9
+    q, k, p, a = _near_tied_pair(b=b)
+    rel = abs(p[0, a] - p[0, b]) / p[0, a]
+    assert 0 < rel < 6e-8, rel
+    hi, lo = (a, b) if p[0, a] > p[0, b] else (b, a)
+    g_hi = p[0][p[0] > p[0, hi]].sum()
+    thr = float(g_hi + 0.5 * p[0, hi])
+    assert 0.5 * p[0, hi] > 1e-4
+    gpu, orc = _run(q, k, thr)
+    res = _assert_parity(gpu, orc, thr)
+    dense = gpu["dense_mask"].reshape(32, 32)
+    assert orc["mask"].reshape(32, 32)[0, hi] == 1 and orc["mask"].reshape(32, 32)[0, lo] == 0
+    assert dense[0, hi] == 1 and dense[0, lo] == 0, res
+
+
+def test_mask_order_below_fp32_resolution_with_d128_and_long_rows():
+    # The same near tie inside long rows (n = 1280 and n = 2100: registers and
+    # LDS row variants) at D = 128.
+    for n in (1280, 2100):
+        b = n - 7
+        q, k, p, a = _near_tied_pair(seed=n, n=n, D=128, b=b)
+        rel = abs(p[0, a] - p[0, b]) / p[0, a]
+        hi, lo = (a, b) if p[0, a] > p[0, b] else (b, a)
+        g_hi = p[0][p[0] > p[0, hi]].sum()
+        thr = float(g_hi + 0.5 * p[0, hi])
+        print(f"[mask] n={n} rel gap {rel:.2e} thr={thr:.6f} half-gap {0.5 * p[0, hi]:.2e}", flush=True)
+        assert 0 < rel < 6e-8, rel
+        gpu, orc = _run(q, k, thr)
+        _assert_parity(gpu, orc, thr)
+        dense = gpu["dense_mask"].reshape(n, n)
+        assert 0.5 * p[0, hi] > 1e-4
+        assert dense[0, hi] == 1 and dense[0, lo] == 0

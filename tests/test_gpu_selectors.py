@@ -178,3 +178,17 @@ def test_topk_720p_full_size():
         assert res["unexplained"] == 0, (bh, res)
     tot = {key: sum(r[key] for r in res_all) for key in res_all[0]}
     print(f"[topk] 720p all {len(res_all)} heads: {tot}", flush=True)
+
+
+def test_topk_order_below_fp32_resolution_is_exact():
+    # Two key blocks whose reduced probabilities differ by ~1e-8 relative (below
+    # fp32 resolution); k chosen so that the cut falls between them: only the
+    # larger one is kept, as in the oracle.
+    from test_gpu_mask import _near_tied_pair
+    b = 9
+    q, k, p, a = _near_tied_pair(b=b)
+    hi, lo = (a, b) if p[0, a] > p[0, b] else (b, a)
+    topk = int((p[0] > p[0, hi]).sum()) + 1
+    gpu, _ = _topk_case(q, k, topk)
+    dense = gpu["dense_mask"].reshape(32, 32)
+    assert dense[0, hi] == 1 and dense[0, lo] == 0

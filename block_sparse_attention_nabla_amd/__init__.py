@@ -148,35 +148,71 @@ def _on_stream(fn):
 
 
 def _check_qkv(name: str, t: torch.Tensor, shape=None):
-    if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
-        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, S, D]")
+    """Shape/dtype/layout of a [B, H, S, D] bf16 input (the device is checked by _check_devices)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_contiguous() \
+            or t.dim() != 4:
+        raise ValueError(f"{name} must be a contiguous bfloat16 tensor [B, H, S, D]")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_tensor(name: str, t, dtypes, shape):
+    """dtype (one of ``dtypes``), exact shape and contiguity of a tensor argument."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    dts = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dts:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dts)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_devices(device: torch.device, **tensors):
+    """Every tensor handed to the library must live on ``device``, a CUDA (HIP) device."""
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a CUDA (HIP) device, got {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _workspace(op, B, H, S, D, N, device, workspace):
     size = nabla_workspace_size(op, B, H, S, D, N)
     if workspace is None:
+        if device.type != "cuda":
+            raise ValueError(f"tensors must be on a CUDA (HIP) device, got {device}")
         workspace = torch.empty(max(size, 1), dtype=torch.uint8, device=device)
+    else:
+        _check_tensor("workspace", workspace, torch.uint8, None)
+        if workspace.numel() < size:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {size}")
+        _check_devices(device, workspace=workspace)
     return workspace, size
 
 
-def _mask_outputs(B, H, n, dev, transpose, dense, out):
+def _mask_outputs(B, H, n, dev, transpose, dense, out, allocate=True):
+    """Check caller-provided mask outputs (shape and dtype first, then device) and
+    allocate the missing ones on ``dev``; with allocate=False, only the shape and
+    dtype checks."""
     out = dict(out or {})
-    res = {}
     keys = [("kv_count", (B, H, n), torch.int32), ("kv_idx", (B, H, n, n), torch.int32)]
     if transpose:
         keys += [("q_count", (B, H, n), torch.int32), ("q_idx", (B, H, n, n), torch.int32)]
     if dense:
         keys += [("dense_mask", (B, H, n, n), torch.uint8)]
+    given = {}
     for key, shape, dtype in keys:
         t = out.get(key)
-        if t is None:
-            t = torch.empty(shape, dtype=dtype, device=dev)
-        if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous():
-            raise ValueError(f"out[{key!r}] must be a contiguous {dtype} tensor of shape {shape}")
-        res[key] = t
-    return res
+        if t is not None:
+            _check_tensor(f"out[{key!r}]", t, dtype, shape)
+            given[f"out[{key!r}]"] = t
+    if not allocate:
+        return None
+    _check_devices(dev, **given)
+    return {key: out[key] if out.get(key) is not None else torch.empty(shape, dtype=dtype, device=dev)
+            for key, shape, dtype in keys}
 
 
 def _sta_ptr(sta: Optional[dict]):
@@ -189,8 +225,10 @@ def _content_mask(fn_name, q, k, select_arg, sta, N, transpose, dense, out, work
     _check_qkv("q", q)
     B, H, S, D = q.shape
     _check_qkv("k", k, q.shape)
-    res = _mask_outputs(B, H, S // N, q.device, transpose, dense, out)
+    _mask_outputs(B, H, S // N, q.device, transpose, dense, out, allocate=False)
     ws, size = _workspace(NABLA_OP_MASK, B, H, S, D, N, q.device, workspace)
+    _check_devices(q.device, k=k)
+    res = _mask_outputs(B, H, S // N, q.device, transpose, dense, out)
     st = getattr(load_library(), fn_name)(
         _ptr(q), _ptr(k), B, H, S, D, N, select_arg, _sta_ptr(sta), _ptr(res["kv_count"]),
         _ptr(res["kv_idx"]), _ptr(res.get("q_count")), _ptr(res.get("q_idx")),
@@ -235,10 +273,9 @@ def nabla_build_sta_mask(B: int, H: int, S: int, sta: dict, device, N: int = BLO
                          stream=None) -> Dict[str, torch.Tensor]:
     """The static STA window alone (section 2.2), as lists for every head."""
     device = torch.device(device)
-    if device.type != "cuda":
-        raise ValueError("device must be a CUDA device")
     if sta is None:
         raise ValueError("the STA-only selector needs the sta window")
+    _check_devices(device)
     res = _mask_outputs(B, H, S // N, device, transpose, dense, out)
     ws, size = _workspace(NABLA_OP_STA_MASK, B, H, S, 0, N, device, workspace)
     if stream is None:
@@ -270,23 +307,22 @@ def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check_qkv("k", k, q.shape)
     _check_qkv("v", v, q.shape)
     n = S // N
-    if kv_count.dtype != torch.int32 or kv_idx.dtype != torch.int32:
-        raise ValueError("kv_count / kv_idx must be int32")
-    if tuple(kv_count.shape) != (B, H, n) or tuple(kv_idx.shape) != (B, H, n, n):
-        raise ValueError("kv_count / kv_idx shapes do not match q")
-    if not (kv_count.is_contiguous() and kv_idx.is_contiguous()):
-        raise ValueError("kv_count / kv_idx must be contiguous")
-    scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    _check_tensor("kv_count", kv_count, torch.int32, (B, H, n))
+    _check_tensor("kv_idx", kv_idx, torch.int32, (B, H, n, n))
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    if o is not None:
+        _check_tensor("o", o, out_dtype, tuple(q.shape))
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, (B, H, S))
+    ws, size = _workspace(NABLA_OP_FWD, B, H, S, D, N, q.device, workspace)
+    _check_devices(q.device, k=k, v=v, kv_count=kv_count, kv_idx=kv_idx, o=o, lse=lse)
+    scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
     if o is None:
         o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    if o.dtype != out_dtype or tuple(o.shape) != tuple(q.shape) or not o.is_contiguous():
-        raise ValueError("o must be a contiguous tensor of q's shape and out_dtype")
     o_dtype = NABLA_DTYPE_FP32 if out_dtype == torch.float32 else NABLA_DTYPE_BF16
     if want_lse and lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    ws, size = _workspace(NABLA_OP_FWD, B, H, S, D, N, q.device, workspace)
     st = load_library().nabla_sparse_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), B, H, S, D, N, _ptr(kv_count), _ptr(kv_idx), scale,
         int(frame_blocks), _ptr(o), o_dtype, _ptr(lse) if want_lse else None, _ptr(ws), ws.numel(), _stream(q, stream))
@@ -307,22 +343,23 @@ def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx
     B, H, S, D = q.shape
     for name, t in (("k", k), ("v", v), ("d_o", d_o)):
         _check_qkv(name, t, q.shape)
-    if o.dtype not in (torch.bfloat16, torch.float32) or tuple(o.shape) != tuple(q.shape) \
-            or not o.is_contiguous() or not o.is_cuda:
-        raise ValueError("o must be a contiguous bf16 or fp32 CUDA tensor of q's shape")
+    _check_tensor("o", o, (torch.bfloat16, torch.float32), tuple(q.shape))
     o_dtype = NABLA_DTYPE_FP32 if o.dtype == torch.float32 else NABLA_DTYPE_BF16
     n = S // N
     for name, t, shp in (("kv_count", kv_count, (B, H, n)), ("kv_idx", kv_idx, (B, H, n, n)),
                          ("q_count", q_count, (B, H, n)), ("q_idx", q_idx, (B, H, n, n))):
-        if t.dtype != torch.int32 or tuple(t.shape) != shp or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous int32 tensor of shape {shp}")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, S]")
+        _check_tensor(name, t, torch.int32, shp)
+    _check_tensor("lse", lse, torch.float32, (B, H, S))
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _check_qkv(name, t, q.shape)
+    ws, size = _workspace(NABLA_OP_BWD, B, H, S, D, N, q.device, workspace)
+    _check_devices(q.device, k=k, v=v, o=o, d_o=d_o, lse=lse, kv_count=kv_count, kv_idx=kv_idx,
+                   q_count=q_count, q_idx=q_idx, dq=dq, dk=dk, dv=dv)
     scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    ws, size = _workspace(NABLA_OP_BWD, B, H, S, D, N, q.device, workspace)
     st = load_library().nabla_sparse_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), o_dtype, _ptr(d_o), _ptr(lse), B, H, S, D, N, _ptr(kv_count),
         _ptr(kv_idx), _ptr(q_count), _ptr(q_idx), scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
@@ -343,13 +380,13 @@ def nabla_block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor,
     _check_qkv("q", q)
     B, H, S, D = q.shape
     _check_qkv("k", k, q.shape)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, S]")
+    _check_tensor("lse", lse, torch.float32, (B, H, S))
     n = S // N
+    if out is not None:
+        _check_tensor("out", out, torch.float32, (B, H, n, n))
+    _check_devices(q.device, k=k, lse=lse, out=out)
     if out is None:
         out = torch.empty((B, H, n, n), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, n, n) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor [B, H, n, n]")
     scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
     st = load_library().nabla_block_mass(_ptr(q), _ptr(k), _ptr(lse), B, H, S, D, N, scale, _ptr(out),
                                          _stream(q, stream))
@@ -362,12 +399,13 @@ def nabla_block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor,
 def nabla_mask_recall(mass: torch.Tensor, kv_count: torch.Tensor, kv_idx: torch.Tensor,
                       N: int = BLOCK_N, *, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per row: block mass inside the kept lists, and inside the best blocks at the same count."""
-    if not mass.is_cuda or mass.dtype != torch.float32 or mass.dim() != 4 or not mass.is_contiguous():
-        raise ValueError("mass must be a contiguous float32 CUDA tensor [B, H, n, n]")
+    if not isinstance(mass, torch.Tensor) or mass.dim() != 4:
+        raise ValueError("mass must be a float32 tensor [B, H, n, n]")
     B, H, n, _ = mass.shape
+    _check_tensor("mass", mass, torch.float32, (B, H, n, n))
     for name, t, shp in (("kv_count", kv_count, (B, H, n)), ("kv_idx", kv_idx, (B, H, n, n))):
-        if t.dtype != torch.int32 or tuple(t.shape) != shp or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous int32 tensor of shape {shp}")
+        _check_tensor(name, t, torch.int32, shp)
+    _check_devices(mass.device, kv_count=kv_count, kv_idx=kv_idx)
     recall = torch.empty((B, H, n), dtype=torch.float32, device=mass.device)
     best = torch.empty_like(recall)
     st = load_library().nabla_mask_recall(_ptr(mass), B, H, n * N, N, _ptr(kv_count), _ptr(kv_idx),
@@ -385,17 +423,18 @@ def nabla_reorder_tokens(x: torch.Tensor, T: int, Hs: int, Ws: int, P: int, inve
     ``x`` is a contiguous CUDA tensor [..., T*Hs*Ws, F] (any dtype): the
     leading dimensions are items, each token's F features one row. Returns the
     tokens in block order (``inverse=False``) or back in raster order."""
-    if not x.is_cuda or not x.is_contiguous() or x.dim() < 2:
-        raise ValueError("x must be a contiguous CUDA tensor [..., T*Hs*Ws, F]")
+    if not isinstance(x, torch.Tensor) or not x.is_contiguous() or x.dim() < 2:
+        raise ValueError("x must be a contiguous tensor [..., T*Hs*Ws, F]")
     S = T * Hs * Ws
     if x.shape[-2] != S:
         raise ValueError(f"x has {x.shape[-2]} tokens, expected T*Hs*Ws = {S}")
     items = x.numel() // max(S * x.shape[-1], 1) if x.numel() else 0
     row_bytes = x.shape[-1] * x.element_size()
+    if out is not None:
+        _check_tensor("out", out, x.dtype, tuple(x.shape))
+    _check_devices(x.device, out=out)
     if out is None:
         out = torch.empty_like(x)
-    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor of x's shape and dtype")
     st = load_library().nabla_reorder_tokens(_ptr(x), _ptr(out), items, T, Hs, Ws, P, row_bytes,
                                              1 if inverse else 0, _stream(x, stream))
     if st != NABLA_OK:

@@ -162,8 +162,12 @@ NABLA_API nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, con
                                      size_t workspace_bytes, void* stream);
 
 /*
- * Block-sparse attention backward: gradients of the forward with the mask held
- * constant (the mask is a piecewise-constant function of Q and K):
+ * Block-sparse attention backward, for training through the NABLA mask: the
+ * mask is built inside the training algorithm of section 3.1 and attention is
+ * trained with it -- fine-tuning (section 4.1) and the 2B-DiT pretraining run of
+ * section 4.3, whose iteration time (10.9 s dense vs 7.5 s sparse) includes this
+ * pass. Gradients of eq. (4) with the mask held constant (the mask is a
+ * piecewise-constant function of Q and K, so it carries no gradient):
  *   P = exp(scale * Q K^T - LSE) on kept blocks, Delta_s = dO_s . O_s,
  *   dV = P^T dO, dP = dO V^T, dS = P * (dP - Delta),
  *   dQ = scale * dS K, dK = scale * dS^T Q.

@@ -112,9 +112,17 @@ def test_dit2b_train_mask_forward_backward():
                                           out["kv_idx"], out["q_count"], out["q_idx"])
     torch.cuda.synchronize()
     rng = np.random.default_rng(6)
-    # Two query blocks (dQ) and two key blocks (dK, dV) sampled in every head.
-    qb = sorted(bh * w.n + int(i) for bh in range(w.B * w.H) for i in rng.choice(w.n, 2, replace=False))
-    kb = sorted(bh * w.n + int(i) for bh in range(w.B * w.H) for i in rng.choice(w.n, 2, replace=False))
+    # Two query blocks (dQ) and two key blocks (dK, dV) sampled in every head, plus
+    # each head's longest loops: the query block with the most kept key blocks
+    # (dQ) and the key block kept by the most query blocks (dK, dV).
+    kvc = out["kv_count"].reshape(w.B * w.H, w.n).cpu().numpy()
+    qc = out["q_count"].reshape(w.B * w.H, w.n).cpu().numpy()
+    qb = sorted({bh * w.n + int(i) for bh in range(w.B * w.H) for i in rng.choice(w.n, 2, replace=False)}
+                | {bh * w.n + int(kvc[bh].argmax()) for bh in range(w.B * w.H)})
+    kb = sorted({bh * w.n + int(i) for bh in range(w.B * w.H) for i in rng.choice(w.n, 2, replace=False)}
+                | {bh * w.n + int(qc[bh].argmax()) for bh in range(w.B * w.H)})
+    print(f"[full] bwd longest loops: dQ up to {kvc.max()} key blocks, dK/dV up to {qc.max()} query blocks",
+          flush=True)
     rdq, rdk, rdv = oracle.attn_bwd(x["q"].float(), x["k"].float(), x["v"].float(), x["do"].float(), mask,
                                     w.N, q_blocks=qb, kv_blocks=kb)
     res = {}

@@ -102,9 +102,12 @@ def test_max_blocks_mask_forward_backward():
     dq, dk, dv = nb.nabla_sparse_attn_bwd(qg, kg, vg, o, dog, lse, out["kv_count"], out["kv_idx"],
                                           out["q_count"], out["q_idx"])
     torch.cuda.synchronize()
-    qb = [5, N_MAX - 2]
+    cnt_row = out["kv_count"][0, 0].cpu().numpy()
+    qb = sorted({5, N_MAX - 2, int(cnt_row.argmax())})  # includes the longest dQ loop
     qc = out["q_count"][0, 0].cpu().numpy()
-    kb = [int(np.argmin(np.where(qc > 0, qc, N_MAX + 1))), 9]  # the oracle's cost grows with q_count
+    # The key block kept by the fewest and by the most query blocks (the longest dK/dV loop).
+    kb = sorted({int(np.argmin(np.where(qc > 0, qc, N_MAX + 1))), 9, int(qc.argmax())})
+    print(f"[max] bwd key blocks {kb} with q_count {[int(qc[j]) for j in kb]}", flush=True)
     rdq, rdk, rdv = oracle.attn_bwd(q.float(), k.float(), v.float(), do.float(), dense, 64,
                                     q_blocks=qb, kv_blocks=kb)
     res = {}

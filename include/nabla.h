@@ -88,7 +88,10 @@ NABLA_API const char* nabla_status_string(nabla_status_t status);
  *   p_il > p_ij -- the sort / cumulative-sum / ">= 1 - thr" binarisation of
  *   steps 8-11 with ties kept together;                            then
  *   keep j also if the STA window of i contains j (when sta != NULL).
- * Everything after the bf16 loads is computed in fp32. Results are written as
+ * Block means are summed exactly (fp64); logits, softmax and masses are fp32,
+ * and the order of the probabilities next to the cut is resolved with fp64
+ * logits, so the kept set follows the exact order of the reduced map (G is
+ * within fp32 rounding of its exact value). Results are written as
  * the compact lists above; q_count/q_idx (needed by the backward pass) and
  * dense_mask (uint8 [B, H, n, n], 1 = kept) are optional (NULL = skip).
  * thr must be finite and >= 0. Every row keeps at least its largest entry.

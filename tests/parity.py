@@ -28,6 +28,9 @@ O_MEAN_ABS = 2e-3
 LSE_MAX_ABS = 1e-3
 GRAD_REL_L2 = 1e-2
 GRAD_MAX_ABS = 5e-2
+# bf16 keeps 8 significant bits: rounding x to bf16 alone moves it by up to
+# 2^-8 |x|, so element-wise gradient checks allow GRAD_MAX_ABS + GRAD_ULP_REL |ref|.
+GRAD_ULP_REL = 2.0 ** -8
 
 
 def compare_masks(gpu_mask: np.ndarray, orc: Dict[str, np.ndarray], thr: float,
@@ -89,7 +92,15 @@ def attn_errors(gpu: np.ndarray, ref: np.ndarray) -> Dict[str, float]:
 
 
 def grad_errors(gpu: np.ndarray, ref: np.ndarray) -> Dict[str, float]:
+    """rel_l2, max_abs, the largest |ref| and the largest error in units of the
+    element-wise bound (GRAD_MAX_ABS + GRAD_ULP_REL |ref|): ``bound_ratio`` <= 1 passes."""
     g = np.asarray(gpu, dtype=np.float64)
     d = g - ref
+    ad = np.abs(d)
     return {"rel_l2": float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30)),
-            "max_abs": float(np.abs(d).max())}
+            "max_abs": float(ad.max()), "max_ref": float(np.abs(ref).max()),
+            "bound_ratio": float((ad / (GRAD_MAX_ABS + GRAD_ULP_REL * np.abs(ref))).max())}
+
+
+def grad_ok(e: Dict[str, float]) -> bool:
+    return e["rel_l2"] <= GRAD_REL_L2 and e["bound_ratio"] <= 1.0

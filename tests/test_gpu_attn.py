@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from parity import (GRAD_MAX_ABS, GRAD_REL_L2, LSE_MAX_ABS, O_MAX_ABS, O_MEAN_ABS, attn_errors,
+from parity import (grad_ok, LSE_MAX_ABS, O_MAX_ABS, O_MEAN_ABS, attn_errors,
                     grad_errors, lists_to_mask)
 
 pytestmark = pytest.mark.gpu
@@ -217,7 +217,7 @@ def _bwd_check(q, k, v, do, lists, mask, tag="", q_blocks=None, kv_blocks=None,
         res[name] = grad_errors(gg[sel], r[sel])
     print(f"[bwd] {tag} {res}", flush=True)
     for name, e in res.items():
-        assert e["rel_l2"] <= GRAD_REL_L2 and e["max_abs"] <= GRAD_MAX_ABS, (name, e)
+        assert grad_ok(e), (name, e)
     return dq, dk, dv
 
 

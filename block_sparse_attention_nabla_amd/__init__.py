@@ -48,6 +48,7 @@ EXPORTED_SYMBOLS = (
     "nabla_build_topk_mask",
     "nabla_build_sta_mask",
     "nabla_sparse_attn_fwd",
+    "nabla_sparse_attn_fwd_static",
     "nabla_sparse_attn_bwd",
     "nabla_reorder_tokens",
     "nabla_block_mass",
@@ -99,6 +100,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nabla_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                           ctypes.c_float, _i32, _vp, _i32, _vp, _vp, ctypes.c_size_t,
                                           _vp]
+    lib.nabla_sparse_attn_fwd_static.restype = ctypes.c_int
+    lib.nabla_sparse_attn_fwd_static.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                                 ctypes.c_float, _i32, _vp, _i32, _vp, _vp]
     lib.nabla_sparse_attn_bwd.restype = ctypes.c_int
     lib.nabla_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
@@ -332,6 +336,45 @@ def nabla_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 @_on_stream
+def nabla_sparse_attn_fwd_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                 kv_count: torch.Tensor, kv_idx: torch.Tensor,
+                                 softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
+                                 o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                                 want_lse: bool = True, out_dtype: torch.dtype = torch.bfloat16,
+                                 frame_blocks: int = 0,
+                                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """nabla_sparse_attn_fwd without a workspace: the library's own device scratch
+    is used (no allocation inside the call; outputs are allocated here only if
+    not passed). Concurrent calls on one GPU race on that scratch."""
+    _check_qkv("q", q)
+    B, H, S, D = q.shape
+    _check_qkv("k", k, q.shape)
+    _check_qkv("v", v, q.shape)
+    n = S // N
+    _check_tensor("kv_count", kv_count, torch.int32, (B, H, n))
+    _check_tensor("kv_idx", kv_idx, torch.int32, (B, H, n, n))
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    if o is not None:
+        _check_tensor("o", o, out_dtype, tuple(q.shape))
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, (B, H, S))
+    _check_devices(q.device, k=k, v=v, kv_count=kv_count, kv_idx=kv_idx, o=o, lse=lse)
+    scale = (1.0 / math.sqrt(D)) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    o_dtype = NABLA_DTYPE_FP32 if out_dtype == torch.float32 else NABLA_DTYPE_BF16
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    st = load_library().nabla_sparse_attn_fwd_static(
+        _ptr(q), _ptr(k), _ptr(v), B, H, S, D, N, _ptr(kv_count), _ptr(kv_idx), scale,
+        int(frame_blocks), _ptr(o), o_dtype, _ptr(lse) if want_lse else None, _stream(q, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, "nabla_sparse_attn_fwd_static")
+    return o, (lse if want_lse else None)
+
+
+@_on_stream
 def nabla_sparse_attn_bwd(q, k, v, o, d_o, lse, kv_count, kv_idx, q_count, q_idx,
                           softmax_scale: Optional[float] = None, N: int = BLOCK_N, *,
                           dq=None, dk=None, dv=None, workspace=None,
@@ -445,6 +488,6 @@ def nabla_reorder_tokens(x: torch.Tensor, T: int, Hs: int, Ws: int, P: int, inve
 __all__ = [
     "LIB_PATH", "BLOCK_N", "EXPORTED_SYMBOLS", "NablaError", "StaWindow", "load_library",
     "nabla_status_string", "nabla_workspace_size", "nabla_build_mask", "nabla_build_topk_mask",
-    "nabla_build_sta_mask", "nabla_sparse_attn_fwd",
+    "nabla_build_sta_mask", "nabla_sparse_attn_fwd", "nabla_sparse_attn_fwd_static",
     "nabla_sparse_attn_bwd", "nabla_reorder_tokens", "nabla_block_mass", "nabla_mask_recall", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD", "NABLA_OP_STA_MASK",
 ]

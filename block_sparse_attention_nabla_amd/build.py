@@ -29,6 +29,7 @@ SOURCES = [
     "attn_bwd.hip",
     "reorder.hip",
     "fidelity.hip",
+    "static_scratch.hip",
 ]
 
 HIPCC_FLAGS = [

@@ -131,6 +131,12 @@ hipError_t launch_mask_recall(const float* mass, int64_t BH, int n, const int32_
                               const int32_t* kv_idx, float* recall, float* best,
                               hipStream_t stream);
 
+// Library-held scratch of the allocation-free forward (static_scratch.hip): the
+// device address of this GPU's copy (the device of `stream`, or the current one
+// for the null stream), looked up once per device.
+constexpr size_t kStaticScratchBytes = NABLA_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch_ptr(hipStream_t stream, void** out);
+
 // Token reordering (block order <-> raster order) of runs of P tokens; see reorder.hip.
 hipError_t launch_reorder(const void* src, void* dst, uint32_t runs, uint32_t cpr, uint32_t P,
                           uint32_t tW, bool inverse, hipStream_t stream);

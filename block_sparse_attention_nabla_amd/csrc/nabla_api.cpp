@@ -184,25 +184,17 @@ nabla_status_t nabla_build_sta_mask(int32_t B, int32_t H, int32_t S, int32_t N,
     return NABLA_OK;
 }
 
-nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t B,
-                                     int32_t H, int32_t S, int32_t D, int32_t N,
-                                     const int32_t* kv_count, const int32_t* kv_idx,
-                                     float softmax_scale, int32_t frame_blocks, void* o,
-                                     int32_t o_dtype, float* lse, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
-    Shape s;
-    nabla_status_t st = check_shape(B, H, S, D, N, &s);
-    if (st != NABLA_OK) return st;
-    if (!q || !k || !v || !o || !kv_count || !kv_idx) return NABLA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return NABLA_ERR_INVALID_ARG;
-    if (!(softmax_scale > 0.0f) || isinf(softmax_scale)) return NABLA_ERR_INVALID_ARG;
-    if (o_dtype != NABLA_DTYPE_BF16 && o_dtype != NABLA_DTYPE_FP32) return NABLA_ERR_INVALID_ARG;
-    if (frame_blocks < 0 || (frame_blocks > 0 && s.n % frame_blocks != 0)) return NABLA_ERR_INVALID_ARG;
-    const FwdWorkspace w = fwd_workspace(s);
-    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
+}  // extern "C"
 
+namespace {
+
+// The forward after its workspace has been provided (caller's or library-held).
+nabla_status_t sparse_attn_fwd(const Shape& s, const void* q, const void* k, const void* v,
+                               const int32_t* kv_count, const int32_t* kv_idx,
+                               float softmax_scale, int32_t frame_blocks, void* o,
+                               int32_t o_dtype, float* lse, void* workspace, hipStream_t hs) {
+    const FwdWorkspace w = fwd_workspace(s);
     int32_t* order = reinterpret_cast<int32_t*>(ws_at(workspace, w.order));
-    hipStream_t hs = as_stream(stream);
     const bool o_fp32 = o_dtype == NABLA_DTYPE_FP32;
     const int n = (int)s.n;
     if (frame_blocks > 0 && n / frame_blocks >= 2) {
@@ -221,6 +213,58 @@ nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v
     NABLA_LAUNCH(launch_attn_fwd(q, k, v, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx, order, sched,
                                  softmax_scale, o, o_fp32, lse, hs));
     return NABLA_OK;
+}
+
+// Argument checks shared by both forward entry points.
+nabla_status_t check_fwd_args(int32_t B, int32_t H, int32_t S, int32_t D, int32_t N, const void* q,
+                              const void* k, const void* v, const int32_t* kv_count,
+                              const int32_t* kv_idx, float softmax_scale, int32_t frame_blocks,
+                              const void* o, int32_t o_dtype, Shape* s) {
+    nabla_status_t st = check_shape(B, H, S, D, N, s);
+    if (st != NABLA_OK) return st;
+    if (!q || !k || !v || !o || !kv_count || !kv_idx) return NABLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return NABLA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || isinf(softmax_scale)) return NABLA_ERR_INVALID_ARG;
+    if (o_dtype != NABLA_DTYPE_BF16 && o_dtype != NABLA_DTYPE_FP32) return NABLA_ERR_INVALID_ARG;
+    if (frame_blocks < 0 || (frame_blocks > 0 && s->n % frame_blocks != 0)) return NABLA_ERR_INVALID_ARG;
+    return NABLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t B,
+                                     int32_t H, int32_t S, int32_t D, int32_t N,
+                                     const int32_t* kv_count, const int32_t* kv_idx,
+                                     float softmax_scale, int32_t frame_blocks, void* o,
+                                     int32_t o_dtype, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    Shape s;
+    nabla_status_t st = check_fwd_args(B, H, S, D, N, q, k, v, kv_count, kv_idx, softmax_scale,
+                                       frame_blocks, o, o_dtype, &s);
+    if (st != NABLA_OK) return st;
+    const FwdWorkspace w = fwd_workspace(s);
+    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return NABLA_ERR_WORKSPACE;
+    return sparse_attn_fwd(s, q, k, v, kv_count, kv_idx, softmax_scale, frame_blocks, o, o_dtype,
+                           lse, workspace, as_stream(stream));
+}
+
+nabla_status_t nabla_sparse_attn_fwd_static(const void* q, const void* k, const void* v, int32_t B,
+                                            int32_t H, int32_t S, int32_t D, int32_t N,
+                                            const int32_t* kv_count, const int32_t* kv_idx,
+                                            float softmax_scale, int32_t frame_blocks, void* o,
+                                            int32_t o_dtype, float* lse, void* stream) {
+    Shape s;
+    nabla_status_t st = check_fwd_args(B, H, S, D, N, q, k, v, kv_count, kv_idx, softmax_scale,
+                                       frame_blocks, o, o_dtype, &s);
+    if (st != NABLA_OK) return st;
+    if (fwd_workspace(s).total > kStaticScratchBytes) return NABLA_ERR_WORKSPACE;
+    hipStream_t hs = as_stream(stream);
+    void* scratch_ptr = nullptr;
+    if (static_scratch_ptr(hs, &scratch_ptr) != hipSuccess) return NABLA_ERR_HIP;
+    return sparse_attn_fwd(s, q, k, v, kv_count, kv_idx, softmax_scale, frame_blocks, o, o_dtype,
+                           lse, scratch_ptr, hs);
 }
 
 nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,

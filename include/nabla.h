@@ -165,6 +165,27 @@ NABLA_API nabla_status_t nabla_sparse_attn_fwd(const void* q, const void* k, con
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free variant of nabla_sparse_attn_fwd, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, checks, kernels and
+ * results (bitwise) without the workspace argument. Its scratch memory -- the
+ * per-head work order and pair counts, 8 * B * H * S / N bytes plus alignment
+ * -- lives in a library-held device array of NABLA_STATIC_SCRATCH_BYTES per
+ * GPU, kept until the process ends; the call allocates and frees nothing.
+ * Shapes that need more scratch than that (B * H * S / N above about one
+ * million blocks) return NABLA_ERR_WORKSPACE before anything is launched.
+ * Calls that overlap on one GPU share the array and race: serialise them
+ * (one stream, or events). The array of the GPU that owns `stream` is used.
+ */
+#define NABLA_STATIC_SCRATCH_BYTES (8u << 20)
+NABLA_API nabla_status_t nabla_sparse_attn_fwd_static(const void* q, const void* k, const void* v,
+                                                      int32_t B, int32_t H, int32_t S, int32_t D,
+                                                      int32_t N, const int32_t* kv_count,
+                                                      const int32_t* kv_idx, float softmax_scale,
+                                                      int32_t frame_blocks, void* o, int32_t o_dtype,
+                                                      float* lse, void* stream);
+
+/*
  * Block-sparse attention backward, for training through the NABLA mask: the
  * mask is built inside the training algorithm of section 3.1 and attention is
  * trained with it -- fine-tuning (section 4.1) and the 2B-DiT pretraining run of

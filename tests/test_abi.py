@@ -222,3 +222,13 @@ def test_fidelity_validation(lib):
     assert rc(None, 1, 2, 1024, 64, P, P, P, P, None) == INVALID
     assert rc(P, 1, 2, 1024, 64, P, P, P, None, None) == INVALID
     assert rc(P, 1, 2, 1024, 32, P, P, P, P, None) == UNSUPPORTED
+
+
+def test_static_forward_rejects_shapes_beyond_its_scratch(lib):
+    # No GPU needed: the shape check fails before any HIP call (dummy aligned pointers).
+    p = ctypes.c_void_p(1 << 20)
+    st = lib.nabla_sparse_attn_fwd_static(p, p, p, 1, 129, 64 * 8192, 64, 64, p, p, 0.125, 0, p, 0,
+                                          None, None)
+    assert st == WORKSPACE
+    st = lib.nabla_sparse_attn_fwd_static(p, p, p, 1, 1, 100, 64, 64, p, p, 0.125, 0, p, 0, None, None)
+    assert st == INVALID  # S % N != 0

@@ -9,7 +9,12 @@ blocks: 4*N*N*D FLOP per kept (query block, key block) pair, divided by the
 step time. Also reported: the forward kernel's own TFLOP/s against the bf16
 MFMA peak (roofline), the speedup over the same kernel run dense, the mask
 stage's HBM GB/s, and the CPU oracle timed on a bounded sample of the same
-workload.
+workload. Under "configs": the other operating point of the layer (80%), the
+layer on the literal std-3 input recipe, and the smaller workloads (the tiny
+threshold sweep, the ~80%-sparse DiT-small layer and its STA union), each with
+the same kernels' dense time, speedup, linearity and load-balance efficiency
+(the time the dense per-pair rate predicts for the kept pairs over the measured
+time), and the CPU oracle timed over each whole small workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--sparsity S] [--no-cpu-baseline]
@@ -354,6 +359,121 @@ def train_step(args, dev, stream) -> dict:
     return res
 
 
+def _time_calls(fn, stream, iters: int) -> float:
+    """Average milliseconds of fn() over `iters` calls, HIP events on `stream`."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def sparse_point(nb, w, q, k, v, thr, stream, iters, fb, dense_ms=None, sta=None, x_host=None,
+                 ws=None, oracle_full=False) -> dict:
+    """Mask + forward timings of one (workload, threshold) on the GPU; with the dense
+    forward time of the same kernel, the speedup, linearity and the load-balance
+    efficiency (the sparse time the dense per-pair rate predicts, over the measured
+    time); optionally the CPU oracle over the whole workload (mask + forward)."""
+    import torch
+    B, H, S, D, n = w.B, w.H, w.S, w.D, w.n
+    dev = q.device
+    if ws is None:
+        ws = {op: torch.empty(nb.nabla_workspace_size(op, B, H, S, D), dtype=torch.uint8, device=dev)
+              for op in (nb.NABLA_OP_MASK, nb.NABLA_OP_FWD)}
+    lists = {"kv_count": torch.empty((B, H, n), dtype=torch.int32, device=dev),
+             "kv_idx": torch.empty((B, H, n, n), dtype=torch.int32, device=dev)}
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+
+    def mask():
+        nb.nabla_build_mask(q, k, thr, sta, out=lists, workspace=ws[nb.NABLA_OP_MASK], stream=stream)
+
+    def fwd():
+        nb.nabla_sparse_attn_fwd(q, k, v, lists["kv_count"], lists["kv_idx"], o=o, lse=lse,
+                                 workspace=ws[nb.NABLA_OP_FWD], stream=stream, frame_blocks=fb)
+    mask_ms = _time_calls(mask, stream, iters)
+    mask()
+    fwd_ms = _time_calls(fwd, stream, iters)
+    counts = lists["kv_count"].reshape(-1)
+    kept = int(counts.sum())
+    density = kept / (B * H * n * n)
+    flops = kept * 4.0 * w.N * w.N * D
+    res = {"thr": round(thr, 6), "block_sparsity": round(1.0 - density, 5),
+           "kept_per_row": {"min": int(counts.min()), "mean": round(kept / (B * H * n), 1),
+                            "max": int(counts.max())},
+           "mask_ms": round(mask_ms, 4), "forward_ms": round(fwd_ms, 4),
+           "forward_tflops": round(flops / (fwd_ms * 1e-3) / 1e12, 2),
+           "frac_bf16_peak": round(flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if dense_ms is not None:
+        speedup = dense_ms / fwd_ms
+        res.update(dense_forward_ms=round(dense_ms, 4), speedup_vs_dense_forward=round(speedup, 3),
+                   speedup_vs_dense_with_mask=round(dense_ms / (mask_ms + fwd_ms), 3),
+                   linearity=round(speedup * density, 3),
+                   load_balance_efficiency=round(density * dense_ms / fwd_ms, 3))
+    if oracle_full and x_host is not None:
+        import oracle
+        qh, kh, vh = (x_host[key].reshape(-1, S, D).float() for key in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        m = oracle.build_mask(qh, kh, w.N, thr, sta=sta)
+        t_mask = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.attn_fwd(qh, kh, vh, m["mask"], w.N)
+        t_fwd = time.perf_counter() - t0
+        okept = int(m["mask"].sum())
+        res["cpu_oracle_full"] = {
+            "seconds": round(t_mask + t_fwd, 3), "mask_s": round(t_mask, 3), "forward_s": round(t_fwd, 3),
+            "tflops": round(okept * 4.0 * w.N * w.N * D / (t_mask + t_fwd) / 1e12, 4),
+            "cores": oracle.num_threads(), "kind": "oracle", "kept_blocks": okept,
+            "gpu_speedup": round((t_mask + t_fwd) * 1e3 / (mask_ms + fwd_ms), 1)}
+    return res
+
+
+def dense_forward_ms(nb, w, q, k, v, stream, iters, fb) -> float:
+    """The same forward kernel with every block kept (thr >= 1 lists)."""
+    import torch
+    B, H, S, D, n = w.B, w.H, w.S, w.D, w.n
+    dev = q.device
+    lists = {"kv_count": torch.empty((B, H, n), dtype=torch.int32, device=dev),
+             "kv_idx": torch.empty((B, H, n, n), dtype=torch.int32, device=dev)}
+    nb.nabla_build_mask(q, k, 1.0, out=lists, stream=stream)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    ws = torch.empty(nb.nabla_workspace_size(nb.NABLA_OP_FWD, B, H, S, D), dtype=torch.uint8, device=dev)
+    return _time_calls(lambda: nb.nabla_sparse_attn_fwd(q, k, v, lists["kv_count"], lists["kv_idx"], o=o,
+                                                        lse=lse, workspace=ws, stream=stream,
+                                                        frame_blocks=fb), stream, iters)
+
+
+def small_configs(nb, dev, stream, args) -> dict:
+    """The smaller workloads on the GPU (mask + forward, dense comparison, load-balance
+    efficiency) with the CPU oracle timed over each whole workload: the threshold
+    sweep of the tiny check, the ~80%-sparse DiT-small layer and the same layer
+    with the STA(11,24,24) union."""
+    import synth
+    out = {}
+    for name in ("tiny", "dit_small", "dit_small_sta"):
+        w = synth.get_workload(name)
+        x = synth.make_inputs(w)
+        q, k, v = (x[key].bfloat16().to(dev) for key in ("q", "k", "v"))
+        fb = 0 if args.no_pairs else (w.Hs // w.P) * (w.Ws // w.P)
+        dense_ms = dense_forward_ms(nb, w, q, k, v, stream, args.config_iters, fb)
+        xh = {key: x[key].bfloat16() for key in ("q", "k", "v")}
+        thrs = w.thresholds()
+        pts = {}
+        for thr in thrs:
+            pts[f"thr={thr:.4f}"] = sparse_point(nb, w, q, k, v, thr, stream, args.config_iters, fb,
+                                                 dense_ms=dense_ms, sta=w.sta_struct(), x_host=xh,
+                                                 oracle_full=not args.no_cpu_baseline)
+        out[name] = {"workload": f"{name}: {w.description}", "frame_blocks": fb, "points": pts}
+        log(f"config {name}: {out[name]}")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -385,6 +505,10 @@ def main() -> int:
     ap.add_argument("--no-reorder", action="store_true",
                     help="skip the token reordering measurement")
     ap.add_argument("--reorder-iters", type=int, default=10)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other operating points and workloads (720p at 80%%, literal "
+                         "std-3 inputs, tiny / dit_small / dit_small_sta with the full CPU oracle)")
+    ap.add_argument("--config-iters", type=int, default=10)
     args = ap.parse_args()
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic, kernel=args.traffic_kernel)))
@@ -574,7 +698,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: {w.description}",
+            "workload": (f"{w.name}: B{B} H{H} D{D}, latent {w.T}x{w.Hs}x{w.Ws} = {S} tokens ({n} blocks), "
+                         f"timed at {100 * sparsity:.0f}% block sparsity (other points under configs)"),
             "B": B, "H": H, "S": S, "D": D, "N": w.N,
             "thr": round(thr, 6), "block_sparsity": round(sparsity, 5),
             "step": "nabla_build_mask + nabla_sparse_attn_fwd (inputs resident in HBM)",
@@ -595,6 +720,8 @@ def main() -> int:
         "speedup_vs_dense_with_mask": (round(dense_ms / (mask_ms + fwd_ms), 3)
                                        if args.dense_iters > 0 else None),
         "linearity": round(speedup * (1 - sparsity), 3) if args.dense_iters > 0 else None,
+        "load_balance_efficiency": (round((1 - sparsity) * dense_ms / fwd_ms, 3)
+                                    if args.dense_iters > 0 else None),
         "roofline": {
             "kernel": FWD_KERNEL if fb else "attn_fwd_kernel",
             "bound": "mfma",
@@ -619,6 +746,19 @@ def main() -> int:
                            "hardware not stated (section 4.3)",
         },
     }
+    if not args.no_configs:
+        configs = {}
+        if w.name == "wan14b_720p":
+            # The other operating point of Table 1 on the same inputs, against the same dense run.
+            other = 0.80 if abs(args.sparsity - 0.90) < 1e-6 else 0.90
+            ws_pair = {nb.NABLA_OP_MASK: ws_mask, nb.NABLA_OP_FWD: ws_fwd}
+            configs[f"wan14b_720p_{int(round(other * 100))}"] = sparse_point(
+                nb, w, q, k, v, w.thr_for(other), stream, args.config_iters, fb,
+                dense_ms=dense_ms if args.dense_iters > 0 else None, ws=ws_pair)
+            log(f"720p at {other}: {configs[f'wan14b_720p_{int(round(other * 100))}']}")
+        out_of_main = small_configs(nb, dev, stream, args)
+        configs.update(out_of_main)
+        result["configs"] = configs
     if not args.no_selectors:
         # Top-k at the CDF rule's mean kept count; STA at Table 1's (18, 24, 24) window.
         topk = max(1, round(kept / (B * H * n)))
@@ -629,6 +769,22 @@ def main() -> int:
         del mass
     if not args.no_reorder:
         result["reorder"] = reorder_bench(w, dev, stream, args.reorder_iters)
+    if not args.no_configs and w.name == "wan14b_720p":
+        # Side figure: the same layer on the literal recipe (pooled-logit std 3),
+        # whose rows are far more peaked (see the input-scale reading).
+        ws3 = {nb.NABLA_OP_MASK: ws_mask, nb.NABLA_OP_FWD: ws_fwd}
+        w3 = synth.get_workload("wan14b_720p_std3")
+        x3 = synth.make_inputs(w3)
+        q3, k3, v3 = (x3[key].to(dev) for key in ("q", "k", "v"))
+        del x3
+        std3 = {"workload": f"{w3.name}: {w3.description}"}
+        for sp in (0.80, 0.90):
+            std3[f"sparsity={sp:.2f}"] = sparse_point(
+                nb, w3, q3, k3, v3, w3.thr_for(sp), stream, args.config_iters, fb,
+                dense_ms=dense_ms if args.dense_iters > 0 else None, ws=ws3)
+        result["configs"]["wan14b_720p_std3"] = std3
+        log(f"std3 side figure: {std3}")
+        del q3, k3, v3
     if not args.no_train:
         del o, lse, lists, ws_mask, ws_fwd, q, k, v
         torch.cuda.empty_cache()

@@ -137,6 +137,11 @@ WORKLOADS: Dict[str, Workload] = {
         name="dit_small_std3", B=1, H=12, D=128, T=11, Hs=32, Ws=32, target_sparsity=(0.80,),
         alpha_rule="std3", seed_base=2,
         description="dit_small inputs scaled to pooled-logit std 3, ~80% sparse"),
+    # The 720p layer on the literal recipe: alpha set so the pooled logits have std 3.
+    "wan14b_720p_std3": Workload(
+        name="wan14b_720p_std3", B=1, H=40, D=128, T=21, Hs=48, Ws=80,
+        target_sparsity=(0.80, 0.90), alpha_rule="std3", seed_base=3,
+        description="wan14b_720p inputs scaled to pooled-logit std 3, 80% and 90% sparse"),
     # 2B video DiT training shape: B=2, H=16, D=128, 16x48x80 = 61440 tokens (960 blocks).
     "dit2b_train": Workload(
         name="dit2b_train", B=2, H=16, D=128, T=16, Hs=48, Ws=80, target_sparsity=(0.85,),

@@ -37,7 +37,8 @@ struct BTile {
     // Row stride (bytes): the tiles are read both row-wise (16 rows x 16 B)
     // and transposed (4 rows x 64 B); a 32-byte pad keeps both at most 2-way.
     static constexpr int RSTB = 2 * D + 32;
-    static constexpr int LOADS = kBlockN * CPR / 128;  // 16-byte chunks per thread per tile
+    template <int NT>
+    static constexpr int loads() { return kBlockN * CPR / NT; }  // 16-byte chunks per thread per tile
 };
 
 // Transposed A operand: rows rbase + 4h + jj (jj = 0..3, and +8 for the upper
@@ -74,6 +75,16 @@ __device__ __forceinline__ void store_t_acc(uint16_t* row_ptr, const f32x16_t* a
             w.y = pack_bf16x2(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
             *reinterpret_cast<uint2*>(row_ptr + 32 * t + 8 * g + 4 * h) = w;
         }
+}
+
+// Mark a value loaded before the main loop as produced here. The compiler's
+// wait-count tracking otherwise carries such loads as possibly outstanding
+// into the loop and waits for them at their first use in every iteration --
+// a wait that, in issue order, also covers the tile prefetch of the previous
+// iteration. With this the wait is taken once, here.
+template <typename T>
+__device__ __forceinline__ void settle(T& x) {
+    asm volatile("" : "+v"(x));
 }
 
 }  // namespace
@@ -122,13 +133,13 @@ __global__ __launch_bounds__(256) void delta_kernel(const void* __restrict__ o,
 }
 
 // Register staging of two 64 x D tiles (A, B) of block `blk` of one head and
-// their write to padded LDS rows. Thread chunk e = tid + 128 i covers row
-// e / CPR, chunk e % CPR.
+// their write to padded LDS rows. Thread chunk e = tid + NT i covers row
+// e / CPR, chunk e % CPR (NT = threads per workgroup).
 #define NABLA_BWD_FETCH(A_SRC, B_SRC, BLK)                                            \
     do {                                                                              \
         const int64_t off_ = (int64_t)(BLK) * kBlockN * D;                            \
         _Pragma("unroll") for (int i_ = 0; i_ < L; ++i_) {                            \
-            const int e_ = tid + 128 * i_;                                            \
+            const int e_ = tid + NT * i_;                                            \
             ra[i_] = *reinterpret_cast<const u32x4_t*>((A_SRC) + off_ + e_ * 8);      \
             rb[i_] = *reinterpret_cast<const u32x4_t*>((B_SRC) + off_ + e_ * 8);      \
         }                                                                             \
@@ -136,7 +147,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const void* __restrict__ o,
 #define NABLA_BWD_STAGE(A_DST, B_DST)                                                 \
     do {                                                                              \
         _Pragma("unroll") for (int i_ = 0; i_ < L; ++i_) {                            \
-            const int e_ = tid + 128 * i_;                                            \
+            const int e_ = tid + NT * i_;                                            \
             const int r_ = e_ / T::CPR, ch_ = e_ % T::CPR;                            \
             *reinterpret_cast<u32x4_t*>((A_DST) + r_ * T::RSTB + 16 * ch_) = ra[i_];  \
             *reinterpret_cast<u32x4_t*>((B_DST) + r_ * T::RSTB + 16 * ch_) = rb[i_];  \
@@ -159,7 +170,8 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     const int32_t* __restrict__ order, XcdSchedule sched, float scale, float scale_log2,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     using T = BTile<D>;
-    constexpr int KK = D / 16, DT = D / 32, L = T::LOADS;
+    constexpr int NT = 128;
+    constexpr int KK = D / 16, DT = D / 32, L = T::template loads<NT>();
     __shared__ __attribute__((aligned(16))) char sQ[kBlockN * T::RSTB];
     __shared__ __attribute__((aligned(16))) char sO[kBlockN * T::RSTB];
     __shared__ __attribute__((aligned(16))) float sL[kBlockN];
@@ -187,6 +199,11 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     for (int kk = 0; kk < KK; ++kk) {
         kf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(k + head + (int64_t)krow * D + 16 * kk + 8 * h));
         vf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(v + head + (int64_t)krow * D + 16 * kk + 8 * h));
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        settle(kf[kk]);
+        settle(vf[kk]);
     }
     f32x16_t dVt[DT], dKt[DT];
 #pragma unroll
@@ -309,13 +326,19 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ for one 64-query block; wave w owns queries 32w .. 32w+31.
-// Per key block j: S^T = K_j Q^T and dP^T = V_j dO^T (A = K_j / V_j rows from
+// dQ for one 64-query block. Four waves split each (query block, key block)
+// pair into 32 x 32 quadrants: wave w takes queries 32 (w / 2) .. +31 and keys
+// 32 (w % 2) .. +31 of every key block. Per key block j:
+// S^T = K_j Q^T and dP^T = V_j dO^T for its quadrant (A = K_j / V_j rows from
 // LDS, B = Q^T / dO^T in registers; accumulator rows = keys), then
-// dQ^T += K_j^T dS^T (A = transposed reads of the K_j tile, B = dS^T).
+// dQ^T += K_j^T dS^T over its 32 keys (A = transposed reads of the K_j tile).
+// The two waves of a query half sum their partial dQ once, through LDS, at
+// the end. Small per-wave state (about 220 registers) lets two workgroups --
+// two waves per SIMD -- share a CU, so one wave's products overlap the other's
+// softmax and LDS reads.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(128) void dq_kernel(
+__global__ __launch_bounds__(256, 2) void dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta, int S, int n,
@@ -323,12 +346,19 @@ __global__ __launch_bounds__(128) void dq_kernel(
     const int32_t* __restrict__ order, XcdSchedule sched, float scale, float scale_log2,
     uint16_t* __restrict__ dq) {
     using T = BTile<D>;
-    constexpr int KK = D / 16, DT = D / 32, L = T::LOADS;
-    __shared__ __attribute__((aligned(16))) char sK[kBlockN * T::RSTB];
-    __shared__ __attribute__((aligned(16))) char sV[kBlockN * T::RSTB];
+    constexpr int NT = 256;
+    constexpr int KK = D / 16, DT = D / 32, L = T::template loads<NT>();
+    // K and V tiles; after the loop, the partial dQ of the key-half-1 waves.
+    constexpr int kTileBytes = kBlockN * T::RSTB;
+    constexpr int kRedBytes = 2 * DT * 16 * kWave * 4;
+    static_assert(kRedBytes <= 2 * kTileBytes, "reduction buffer exceeds the tile buffers");
+    __shared__ __attribute__((aligned(16))) char sKV[2 * kTileBytes];
+    char* const sK = sKV;
+    char* const sV = sKV + kTileBytes;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, c = lane & 31;
+    const int kh = wave & 1, qh = wave >> 1;
     const int64_t item = scheduled_item(sched, order, blockIdx.x);
     if (item < 0) return;  // padding slot (whole workgroup)
     const int64_t bh = item / n;
@@ -337,50 +367,57 @@ __global__ __launch_bounds__(128) void dq_kernel(
     cnt = cnt < 0 ? 0 : (cnt > n ? n : cnt);
     const int32_t* list = kv_idx + item * (int64_t)n;
     const int64_t head = bh * (int64_t)S * D;
-    const uint16_t* kh = k + head;
-    const uint16_t* vh = v + head;
+    const uint16_t* kh_ptr = k + head;
+    const uint16_t* vh_ptr = v + head;
 
-    const int qrow = qb * kBlockN + wave * 32 + c;
+    const int qrow = qb * kBlockN + qh * 32 + c;
     bf16x8_t qf[KK], dof[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         qf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(q + head + (int64_t)qrow * D + 16 * kk + 8 * h));
         dof[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(d_o + head + (int64_t)qrow * D + 16 * kk + 8 * h));
     }
-    const float l2 = lse[bh * (int64_t)S + qrow] * kLog2e;
-    const float del = delta[bh * (int64_t)S + qrow];
+    float l2 = lse[bh * (int64_t)S + qrow] * kLog2e;
+    float del = delta[bh * (int64_t)S + qrow];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        settle(qf[kk]);
+        settle(dof[kk]);
+    }
+    settle(l2);
+    settle(del);
     f32x16_t dQt[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) dQt[t] = zero16();
 
-    const char* krow_base = sK + c * T::RSTB + 16 * h;  // row 32 kt + c, bytes 32 kk + 16 h
-    const char* vrow_base = sV + c * T::RSTB + 16 * h;
+    // Rows 32 kh + c of the K / V tiles, bytes 32 kk + 16 h.
+    const char* krow_base = sK + (32 * kh + c) * T::RSTB + 16 * h;
+    const char* vrow_base = sV + (32 * kh + c) * T::RSTB + 16 * h;
     const char* ktr = tr_lane_base(sK, lane, T::RSTB);
 
     u32x4_t ra[L], rb[L];
     if (cnt > 0) {
         int j0 = list[0];
         j0 = (unsigned)j0 < (unsigned)n ? j0 : 0;
-        NABLA_BWD_FETCH(kh, vh, j0);
+        NABLA_BWD_FETCH(kh_ptr, vh_ptr, j0);
         NABLA_BWD_STAGE(sK, sV);
         if (cnt > 1) {
             int j1 = list[1];
             j1 = (unsigned)j1 < (unsigned)n ? j1 : 0;
-            NABLA_BWD_FETCH(kh, vh, j1);
+            NABLA_BWD_FETCH(kh_ptr, vh_ptr, j1);
         }
         __syncthreads();
     }
     for (int it = 0; it < cnt; ++it) {
-        uint32_t dsw[2][8];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            // S^T and dP^T tiles: rows = keys 32 kt + c_row(r, h), column = query c.
+        uint32_t dsw[8];
+        {
+            // S^T and dP^T quadrant: rows = keys 32 kh + c_row(r, h), column = query c.
             f32x16_t sc = zero16(), dp = zero16();
             {
                 bf16x8_t a[KK];
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(krow_base + 32 * kt * T::RSTB + 32 * kk));
+                    a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(krow_base + 32 * kk));
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) sc = mfma_32x32x16(a[kk], qf[kk], sc);
             }
@@ -388,7 +425,7 @@ __global__ __launch_bounds__(128) void dq_kernel(
                 bf16x8_t a[KK];
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(vrow_base + 32 * kt * T::RSTB + 32 * kk));
+                    a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(vrow_base + 32 * kk));
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) dp = mfma_32x32x16(a[kk], dof[kk], dp);
             }
@@ -398,31 +435,45 @@ __global__ __launch_bounds__(128) void dq_kernel(
                 dp[r] = p * (dp[r] - del);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dsw[kt][e] = pack_bf16x2(dp[2 * e], dp[2 * e + 1]);
+            for (int e = 0; e < 8; ++e) dsw[e] = pack_bf16x2(dp[2 * e], dp[2 * e + 1]);
         }
-        // dQ^T += K^T dS^T: slot s of B is key 32 kt + 16 u + 8 (s/4) + 4 h + s%4.
+        // dQ^T += K^T dS^T: slot s of B is key 32 kh + 16 u + 8 (s/4) + 4 h + s%4.
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8_t bs = as_bf16x8(make_uint4(dsw[4 * u], dsw[4 * u + 1], dsw[4 * u + 2], dsw[4 * u + 3]));
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8_t bs = as_bf16x8(make_uint4(dsw[kt][4 * u], dsw[kt][4 * u + 1],
-                                                         dsw[kt][4 * u + 2], dsw[kt][4 * u + 3]));
-#pragma unroll
-                for (int t = 0; t < DT; ++t)
-                    dQt[t] = mfma_32x32x16(tr_operand<T::RSTB>(ktr, 32 * kt + 16 * u, t), bs, dQt[t]);
-            }
+            for (int t = 0; t < DT; ++t)
+                dQt[t] = mfma_32x32x16(tr_operand<T::RSTB>(ktr, 32 * kh + 16 * u, t), bs, dQt[t]);
+        }
         if (it + 1 < cnt) {
             __syncthreads();  // every wave is done with this key block's tiles
             NABLA_BWD_STAGE(sK, sV);
             if (it + 2 < cnt) {
                 int j2 = list[it + 2];
                 j2 = (unsigned)j2 < (unsigned)n ? j2 : 0;
-                NABLA_BWD_FETCH(kh, vh, j2);
+                NABLA_BWD_FETCH(kh_ptr, vh_ptr, j2);
             }
             __syncthreads();
         }
     }
-    store_t_acc<DT>(dq + head + (int64_t)qrow * D, dQt, scale, h);
+    // Sum the two key halves: the kh = 1 wave parks its accumulators in LDS in
+    // register order (lane-contiguous words), the kh = 0 wave adds and stores.
+    __syncthreads();  // tiles no longer read
+    float* red = reinterpret_cast<float*>(sKV) + qh * (DT * 16 * kWave);
+    if (kh == 1) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(t * 16 + r) * kWave + lane] = dQt[t][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dQt[t][r] += red[(t * 16 + r) * kWave + lane];
+        store_t_acc<DT>(dq + head + (int64_t)qrow * D, dQt, scale, h);
+    }
 }
 
 #undef NABLA_BWD_FETCH
@@ -473,11 +524,11 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
     const unsigned grid = (unsigned)sched.grid;
     const float sl2 = softmax_scale * kLog2e;
     if (D == 128)
-        dq_kernel<128><<<grid, 128, 0, stream>>>(
+        dq_kernel<128><<<grid, 256, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse,
             delta, S, n, kv_count, kv_idx, order, sched, softmax_scale, sl2, (uint16_t*)dq);
     else
-        dq_kernel<64><<<grid, 128, 0, stream>>>(
+        dq_kernel<64><<<grid, 256, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse,
             delta, S, n, kv_count, kv_idx, order, sched, softmax_scale, sl2, (uint16_t*)dq);
     return hipGetLastError();

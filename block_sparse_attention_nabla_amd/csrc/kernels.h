@@ -60,22 +60,41 @@ hipError_t launch_transpose(const uint32_t* bits, int64_t BH, int n, int words_p
 // [0, maxc] (maxc <= NABLA_MAX_BLOCKS; others are clamped): order[h*items + p] =
 // item id (h*items + i) of head h's p-th item, counts descending (ties in any order).
 hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int items, int maxc,
-                            int32_t* order, hipStream_t stream);
+                            int32_t* order, int32_t* claim, hipStream_t stream);
 
-// XCD-aware launch geometry (see schedule.hip): heads are split into `parts`
-// interleaved shares so that `units` = BH * parts is a multiple of the 8 XCDs;
-// workgroup b runs on XCD b % 8 and serves unit x + 8 * (m / cap), position
-// m % cap, with x = b % 8, m = b / 8.
+// XCD-aware launch geometry (see schedule.hip). Three ways to map workgroup b
+// to a work item of a per-head longest-first order:
+//  kSchedStatic   heads are split into `parts` interleaved shares so that
+//                 `units` = BH * parts is a multiple of the 8 XCDs; workgroup b
+//                 runs on XCD b % 8 and serves unit x + 8 * (m / cap), position
+//                 part + parts * (m % cap), with x = b % 8, m = b / 8.
+//  kSchedClaim    the same head-to-XCD mapping, but the `parts` XCDs that share
+//                 a head take its positions in longest-first order from a
+//                 per-head counter (claim[head], zeroed by the ordering kernel)
+//                 as their workgroups start, so a faster XCD takes more items;
+//                 cap carries a quarter more workgroups than items, and the
+//                 ones that find a head exhausted exit at once.
+//  kSchedPosMajor small problems (whose K/V fit the Infinity Cache): position
+//                 p of every head before position p + 1 of any head, so the
+//                 longest items of all heads start first.
+enum : int { kSchedStatic = 0, kSchedClaim = 1, kSchedPosMajor = 2 };
 struct XcdSchedule {
     int parts;
     int64_t units;
     int cap;
-    int n;
+    int n;  // items per head
     int64_t grid;
+    int mode;
+    int64_t bh;
+    int32_t* claim;
 };
 XcdSchedule make_schedule(int64_t BH, int n);
+// Balanced schedule for an attention launch: kSchedPosMajor when the problem is
+// small, else kSchedClaim with the per-head counters `claim` (BH int32).
+XcdSchedule make_balanced_schedule(int64_t BH, int n, int64_t kv_bytes_per_head, int32_t* claim);
 
-// Slot (head * n + position) of workgroup b, or -1 for a padding slot.
+// Slot (head * n + position) of workgroup b under kSchedStatic, or -1 for a
+// padding slot.
 __device__ __forceinline__ int64_t scheduled_slot(const XcdSchedule& s, int64_t b) {
     const int64_t x = b % 8, m = b / 8;
     const int64_t unit = x + 8 * (m / s.cap);
@@ -86,9 +105,24 @@ __device__ __forceinline__ int64_t scheduled_slot(const XcdSchedule& s, int64_t 
     return head * s.n + pos;
 }
 
-// Work item of workgroup b (through a per-head order), or -1 for a padding slot.
+// Work item of workgroup b (through a per-head order), or -1 for a workgroup
+// with nothing to do. Every thread of the workgroup must call it (kSchedClaim
+// broadcasts the claimed position through LDS).
 __device__ __forceinline__ int64_t scheduled_item(const XcdSchedule& s, const int32_t* order,
                                                   int64_t b) {
+    if (s.mode == kSchedPosMajor) {
+        const int64_t pos = b / s.bh, head = b % s.bh;
+        return pos < s.n ? order[head * s.n + pos] : -1;
+    }
+    if (s.mode == kSchedClaim) {
+        __shared__ int claimed;
+        const int64_t m = b / 8;
+        const int64_t head = (b % 8 + 8 * (m / s.cap)) / s.parts;
+        if (threadIdx.x == 0) claimed = atomicAdd(s.claim + head, 1);
+        __syncthreads();
+        const int64_t pos = claimed;
+        return pos < s.n ? order[head * s.n + pos] : -1;
+    }
     const int64_t slot = scheduled_slot(s, b);
     return slot < 0 ? -1 : order[slot];
 }

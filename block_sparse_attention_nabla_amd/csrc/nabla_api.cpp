@@ -195,21 +195,23 @@ nabla_status_t sparse_attn_fwd(const Shape& s, const void* q, const void* k, con
                                int32_t o_dtype, float* lse, void* workspace, hipStream_t hs) {
     const FwdWorkspace w = fwd_workspace(s);
     int32_t* order = reinterpret_cast<int32_t*>(ws_at(workspace, w.order));
+    int32_t* claim = reinterpret_cast<int32_t*>(ws_at(workspace, w.claim));
     const bool o_fp32 = o_dtype == NABLA_DTYPE_FP32;
     const int n = (int)s.n;
+    const int64_t kv_bytes = 2 * s.S * s.D * (int64_t)sizeof(uint16_t);  // one head's K and V
     if (frame_blocks > 0 && n / frame_blocks >= 2) {
         // Pairs of query blocks (i, i + F): the same tile in consecutive frames.
         const int np = pair_count(n, frame_blocks);
         int32_t* pc = reinterpret_cast<int32_t*>(ws_at(workspace, w.counts));
-        const XcdSchedule sched = make_schedule(s.BH, np);
+        const XcdSchedule sched = make_balanced_schedule(s.BH, np, kv_bytes, claim);
         NABLA_LAUNCH(launch_pair_counts(kv_count, s.BH, n, frame_blocks, pc, hs));
-        NABLA_LAUNCH(launch_lpt_order(pc, s.BH, np, n, order, hs));
+        NABLA_LAUNCH(launch_lpt_order(pc, s.BH, np, n, order, claim, hs));
         NABLA_LAUNCH(launch_attn_fwd_pairs(q, k, v, s.BH, (int)s.S, (int)s.D, frame_blocks, kv_count,
                                            kv_idx, order, sched, softmax_scale, o, o_fp32, lse, hs));
         return NABLA_OK;
     }
-    const XcdSchedule sched = make_schedule(s.BH, n);
-    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, n, n, order, hs));
+    const XcdSchedule sched = make_balanced_schedule(s.BH, n, kv_bytes, claim);
+    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, n, n, order, claim, hs));
     NABLA_LAUNCH(launch_attn_fwd(q, k, v, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx, order, sched,
                                  softmax_scale, o, o_fp32, lse, hs));
     return NABLA_OK;
@@ -291,13 +293,16 @@ nabla_status_t nabla_sparse_attn_bwd(const void* q, const void* k, const void* v
     float* delta = reinterpret_cast<float*>(ws_at(workspace, w.delta));
     int32_t* order_q = reinterpret_cast<int32_t*>(ws_at(workspace, w.order_q));
     int32_t* order_kv = reinterpret_cast<int32_t*>(ws_at(workspace, w.order_kv));
+    int32_t* claim = reinterpret_cast<int32_t*>(ws_at(workspace, w.claim));
     hipStream_t hs = as_stream(stream);
     NABLA_LAUNCH(launch_bwd_delta(o, o_dtype == NABLA_DTYPE_FP32, d_o, s.BH * s.S, (int)s.D, delta, hs));
-    const XcdSchedule sched = make_schedule(s.BH, (int)s.n);
-    NABLA_LAUNCH(launch_lpt_order(q_count, s.BH, (int)s.n, (int)s.n, order_kv, hs));
+    // Q, K, V and dO of one head are read by each backward kernel.
+    const int64_t head_bytes = 4 * s.S * s.D * (int64_t)sizeof(uint16_t);
+    const XcdSchedule sched = make_balanced_schedule(s.BH, (int)s.n, head_bytes, claim);
+    NABLA_LAUNCH(launch_lpt_order(q_count, s.BH, (int)s.n, (int)s.n, order_kv, claim, hs));
     NABLA_LAUNCH(launch_bwd_dkdv(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, q_count, q_idx,
                                  order_kv, sched, softmax_scale, dk, dv, hs));
-    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, (int)s.n, (int)s.n, order_q, hs));
+    NABLA_LAUNCH(launch_lpt_order(kv_count, s.BH, (int)s.n, (int)s.n, order_q, claim, hs));
     NABLA_LAUNCH(launch_bwd_dq(q, k, v, d_o, lse, delta, s.BH, (int)s.S, (int)s.D, kv_count, kv_idx,
                                order_q, sched, softmax_scale, dq, hs));
     return NABLA_OK;

@@ -11,7 +11,13 @@
 // second, fourth or eighth item of its longest-first order).
 // (2) Load balance: kept-block counts differ a lot between query blocks (the
 // CDF rule keeps few blocks for peaked rows and many for flat ones), so
-// within a head the longest items start first.
+// within a head the longest items start first. XCDs also differ in speed
+// (measured: the same number of block steps takes up to 4% longer on some
+// XCDs than on others), so the XCDs that share a head take its items from a
+// counter as they start rather than by a fixed interleave. Small problems,
+// whose K/V all fit the Infinity Cache and whose few workgroups per CU make
+// the longest items set the kernel's length, start the longest items of
+// every head first instead.
 
 #include "common.h"
 #include "kernels.h"
@@ -22,15 +28,17 @@ constexpr int kLptThreads = 1024;
 
 // One workgroup per head: counting sort of the head's `items` items by count
 // (descending; counts clamped to [0, n]). order[h*items + p] = global item id
-// of the head's p-th item.
+// of the head's p-th item. Also zeroes the head's claim counter, if any.
 __global__ __launch_bounds__(kLptThreads) void head_lpt_kernel(const int32_t* __restrict__ counts,
                                                                int items, int n,
-                                                               int32_t* __restrict__ order) {
+                                                               int32_t* __restrict__ order,
+                                                               int32_t* __restrict__ claim) {
     __shared__ int hist[NABLA_MAX_BLOCKS + 1];
     __shared__ int chunk_sum[kLptThreads];
     const int t = threadIdx.x;
     const int64_t base = (int64_t)blockIdx.x * items;
     const int nb = n + 1;  // count values 0..n
+    if (claim && t == 0) claim[blockIdx.x] = 0;
     for (int c = t; c < nb; c += kLptThreads) hist[c] = 0;
     __syncthreads();
     for (int it = t; it < items; it += kLptThreads) {
@@ -69,8 +77,8 @@ __global__ __launch_bounds__(kLptThreads) void head_lpt_kernel(const int32_t* __
 }
 
 hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int items, int maxc,
-                            int32_t* order, hipStream_t stream) {
-    head_lpt_kernel<<<(unsigned)BH, kLptThreads, 0, stream>>>(counts, items, maxc, order);
+                            int32_t* order, int32_t* claim, hipStream_t stream) {
+    head_lpt_kernel<<<(unsigned)BH, kLptThreads, 0, stream>>>(counts, items, maxc, order, claim);
     return hipGetLastError();
 }
 
@@ -91,6 +99,30 @@ XcdSchedule make_schedule(int64_t BH, int n) {
     s.cap = (n + s.parts - 1) / s.parts;     // positions per part
     s.n = n;
     s.grid = s.units * s.cap;
+    s.mode = kSchedStatic;
+    s.bh = BH;
+    s.claim = nullptr;
+    return s;
+}
+
+// Problems up to this many work items whose K/V (all heads) fit this many
+// bytes use the position-major order.
+constexpr int64_t kPosMajorItems = 16384;
+constexpr int64_t kPosMajorBytes = 128ll << 20;
+
+XcdSchedule make_balanced_schedule(int64_t BH, int n, int64_t kv_bytes_per_head, int32_t* claim) {
+    XcdSchedule s = make_schedule(BH, n);
+    if (BH * n <= kPosMajorItems && BH * kv_bytes_per_head <= kPosMajorBytes) {
+        s.mode = kSchedPosMajor;
+        s.grid = BH * n;
+        return s;
+    }
+    if (claim) {
+        s.mode = kSchedClaim;
+        s.claim = claim;
+        s.cap = (5 * n + 4 * s.parts - 1) / (4 * s.parts);  // a quarter to spare
+        s.grid = s.units * s.cap;
+    }
     return s;
 }
 

@@ -64,7 +64,8 @@ FwdWorkspace fwd_workspace(const Shape& s) {
     FwdWorkspace w;
     w.order = 0;
     w.counts = align256((size_t)s.BH * s.n * sizeof(int32_t));
-    w.total = w.counts + align256((size_t)s.BH * s.n * sizeof(int32_t));
+    w.claim = w.counts + align256((size_t)s.BH * s.n * sizeof(int32_t));
+    w.total = w.claim + align256((size_t)s.BH * sizeof(int32_t));
     return w;
 }
 
@@ -73,7 +74,8 @@ BwdWorkspace bwd_workspace(const Shape& s) {
     w.delta = 0;
     w.order_q = align256((size_t)s.BH * s.S * sizeof(float));
     w.order_kv = w.order_q + align256((size_t)s.BH * s.n * sizeof(int32_t));
-    w.total = w.order_kv + align256((size_t)s.BH * s.n * sizeof(int32_t));
+    w.claim = w.order_kv + align256((size_t)s.BH * s.n * sizeof(int32_t));
+    w.total = w.claim + align256((size_t)s.BH * sizeof(int32_t));
     return w;
 }
 

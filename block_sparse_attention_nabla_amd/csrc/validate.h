@@ -23,10 +23,10 @@ struct StaWorkspace {
     int words_per_row;
 };
 struct FwdWorkspace {
-    size_t order, counts, total;
+    size_t order, counts, claim, total;
 };
 struct BwdWorkspace {
-    size_t delta, order_q, order_kv, total;
+    size_t delta, order_q, order_kv, claim, total;
 };
 
 nabla_status_t check_shape(int32_t B, int32_t H, int32_t S, int32_t D, int32_t N, Shape* out);

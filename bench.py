@@ -54,16 +54,22 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # given (the default), the one-block kernel with --no-pairs.
 FWD_KERNEL = "attn_fwd_pair_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan14b_720p_traffic.json")
-FWD_SOURCE = os.path.join(ROOT, "block_sparse_attention_nabla_amd", "csrc", "attn_fwd.hip")
+# Everything the forward kernel's code and work order come from: counters taken
+# on other sources are not reported.
+FWD_SOURCES = [os.path.join(ROOT, "block_sparse_attention_nabla_amd", "csrc", f)
+               for f in ("attn_fwd.hip", "kernels.h", "common.h", "schedule.hip")]
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(launch_flops: float):
@@ -73,7 +79,7 @@ def measured_traffic(launch_flops: float):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != source_hash(FWD_SOURCE):
+    if t.get("kernel_source_sha256_16") != source_hash(FWD_SOURCES):
         return None
     return t.get("bytes_per_launch")
 
@@ -115,7 +121,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, kernel: str = FWD_KERNEL) 
         "calibration": {"copy_bytes": CALIB_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
                         "raw_copy_fetch_kb": max(f["copy"]), "raw_copy_write_kb": max(wr["copy"])},
         "launches": {"fetch": len(f["fwd"]), "write": len(wr["fwd"])},
-        "kernel_source_sha256_16": source_hash(FWD_SOURCE),
+        "kernel_source_sha256_16": source_hash(FWD_SOURCES),
     }
     if kernel != FWD_KERNEL:
         return res
@@ -756,6 +762,16 @@ def main() -> int:
                 nb, w, q, k, v, w.thr_for(other), stream, args.config_iters, fb,
                 dense_ms=dense_ms if args.dense_iters > 0 else None, ws=ws_pair)
             log(f"720p at {other}: {configs[f'wan14b_720p_{int(round(other * 100))}']}")
+            # The STA-union workload at the layer's own shape: the 90% CDF mask of the same
+            # inputs OR the STA(11, 24, 24) window (per-row counts 24-535 blocks).
+            sta720 = dict(T=w.T, Hs=w.Hs, Ws=w.Ws, P=w.P, win_t=11, win_h=24, win_w=24)
+            configs["wan14b_720p_90_sta"] = sparse_point(
+                nb, w, q, k, v, w.thr_for(0.90), stream, args.config_iters, fb,
+                dense_ms=dense_ms if args.dense_iters > 0 else None, ws=ws_pair, sta=sta720)
+            configs["wan14b_720p_90_sta"]["workload"] = (
+                "wan14b_720p inputs, NABLA(thr of 90%) OR STA(11,24,24) (temporal +-5 frames, "
+                "spatial 3x3 tiles)")
+            log(f"720p STA union: {configs['wan14b_720p_90_sta']}")
         out_of_main = small_configs(nb, dev, stream, args)
         configs.update(out_of_main)
         result["configs"] = configs

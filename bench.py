@@ -439,6 +439,31 @@ def sparse_point(nb, w, q, k, v, thr, stream, iters, fb, dense_ms=None, sta=None
     return res
 
 
+def dense_sdpa_ms(q, k, v, stream, iters):
+    """torch.nn.functional.scaled_dot_product_attention on the same bf16 Q, K, V with
+    the flash backend forced (no fallback to the unfused math path); None if that
+    backend is unavailable for the shape."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    try:
+        with torch.cuda.stream(stream), sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            F.scaled_dot_product_attention(q, k, v)
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
+            for e in ev:
+                e[0].record(stream)
+                F.scaled_dot_product_attention(q, k, v)
+                e[1].record(stream)
+            torch.cuda.synchronize()
+    except RuntimeError as exc:
+        log(f"torch SDPA flash backend unavailable: {exc}")
+        return None
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / iters
+    log(f"torch SDPA (flash) dense forward {ms:.2f} ms")
+    return ms
+
+
 def dense_forward_ms(nb, w, q, k, v, stream, iters, fb) -> float:
     """The same forward kernel with every block kept (thr >= 1 lists)."""
     import torch
@@ -658,6 +683,7 @@ def main() -> int:
         log(f"dense forward {dense_ms:.2f} ms ({dense_flops / dense_ms / 1e9:.1f} TFLOP/s); "
             f"speedup {speedup:.2f}x at density {1 - sparsity:.4f} (linearity {speedup * (1 - sparsity):.3f})")
         del dense_lists
+    sdpa_ms = dense_sdpa_ms(q, k, v, stream, args.dense_iters) if args.dense_iters > 0 else None
 
     # Mask fidelity: true block mass of dense attention (the dense run above left
     # the dense LSE in `lse`), and the recall of the 90% CDF lists.
@@ -725,6 +751,10 @@ def main() -> int:
         "speedup_vs_dense_forward": round(speedup, 3) if args.dense_iters > 0 else None,
         "speedup_vs_dense_with_mask": (round(dense_ms / (mask_ms + fwd_ms), 3)
                                        if args.dense_iters > 0 else None),
+        # PyTorch's own dense attention on the same Q, K, V (flash backend forced): an
+        # independent dense baseline beside this library's kernel run dense.
+        "dense_torch_sdpa_ms": round(sdpa_ms, 3) if sdpa_ms else None,
+        "speedup_vs_torch_sdpa_dense": round(sdpa_ms / fwd_ms, 3) if sdpa_ms else None,
         "linearity": round(speedup * (1 - sparsity), 3) if args.dense_iters > 0 else None,
         "load_balance_efficiency": (round((1 - sparsity) * dense_ms / fwd_ms, 3)
                                     if args.dense_iters > 0 else None),

@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
     nabla_reorder_tokens(x, T, Hs, Ws, P, inverse=False) -> reordered copy
     nabla_block_mass(q, k, lse)                      -> dense block masses [B,H,n,n]
     nabla_mask_recall(mass, kv_count, kv_idx)        -> (recall, best_recall) per row
+    nabla_check_lists(count, idx)                    -> number of malformed list rows
     nabla_workspace_size(op, B, H, S, D, N), nabla_status_string(code)
 
 Streams: every entry point launches on ``stream`` (a torch.cuda.Stream), else on
@@ -53,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "nabla_reorder_tokens",
     "nabla_block_mass",
     "nabla_mask_recall",
+    "nabla_check_lists",
 )
 
 
@@ -112,6 +114,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      _vp]
     lib.nabla_mask_recall.restype = ctypes.c_int
     lib.nabla_mask_recall.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.nabla_check_lists.restype = ctypes.c_int
+    lib.nabla_check_lists.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
     lib.nabla_reorder_tokens.restype = ctypes.c_int
     lib.nabla_reorder_tokens.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int64,
                                          _i32, _vp]
@@ -459,6 +463,26 @@ def nabla_mask_recall(mass: torch.Tensor, kv_count: torch.Tensor, kv_idx: torch.
 
 
 @_on_stream
+def nabla_check_lists(count: torch.Tensor, idx: torch.Tensor, N: int = BLOCK_N, *,
+                      stream=None) -> int:
+    """Number of rows whose list is malformed (count outside [0, n]; an entry outside
+    [0, n) or not larger than its predecessor among the first count entries). Waits
+    for the stream to reach the check (it returns a host integer)."""
+    if not isinstance(count, torch.Tensor) or count.dim() != 3:
+        raise ValueError("count must be an int32 tensor [B, H, n]")
+    B, H, n = count.shape
+    _check_tensor("count", count, torch.int32, (B, H, n))
+    _check_tensor("idx", idx, torch.int32, (B, H, n, n))
+    _check_devices(count.device, idx=idx)
+    bad = torch.empty((), dtype=torch.int32, device=count.device)
+    st = load_library().nabla_check_lists(_ptr(count), _ptr(idx), B, H, n * N, N, _ptr(bad),
+                                          _stream(count, stream))
+    if st != NABLA_OK:
+        raise NablaError(st, "nabla_check_lists")
+    return int(bad.item())
+
+
+@_on_stream
 def nabla_reorder_tokens(x: torch.Tensor, T: int, Hs: int, Ws: int, P: int, inverse: bool = False,
                          *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Token reordering of section 3.1.1 (Figure 3) or its inverse, out of place.
@@ -489,5 +513,5 @@ __all__ = [
     "LIB_PATH", "BLOCK_N", "EXPORTED_SYMBOLS", "NablaError", "StaWindow", "load_library",
     "nabla_status_string", "nabla_workspace_size", "nabla_build_mask", "nabla_build_topk_mask",
     "nabla_build_sta_mask", "nabla_sparse_attn_fwd", "nabla_sparse_attn_fwd_static",
-    "nabla_sparse_attn_bwd", "nabla_reorder_tokens", "nabla_block_mass", "nabla_mask_recall", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD", "NABLA_OP_STA_MASK",
+    "nabla_sparse_attn_bwd", "nabla_reorder_tokens", "nabla_block_mass", "nabla_mask_recall", "nabla_check_lists", "NABLA_OP_MASK", "NABLA_OP_FWD", "NABLA_OP_BWD", "NABLA_OP_STA_MASK",
 ]

@@ -161,6 +161,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 // dense LSE; per-row recall of block lists and of the best blocks at equal count.
 hipError_t launch_block_mass(const void* q, const void* k, const float* lse, int64_t BH, int S,
                              int D, float softmax_scale, float* mass, hipStream_t stream);
+// Rows with a malformed list (see nabla_check_lists) counted into *bad (zeroed first).
+hipError_t launch_check_lists(const int32_t* count, const int32_t* idx, int64_t rows, int n,
+                              int32_t* bad, hipStream_t stream);
 hipError_t launch_mask_recall(const float* mass, int64_t BH, int n, const int32_t* kv_count,
                               const int32_t* kv_idx, float* recall, float* best,
                               hipStream_t stream);

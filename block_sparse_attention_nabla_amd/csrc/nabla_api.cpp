@@ -334,6 +334,16 @@ nabla_status_t nabla_mask_recall(const float* mass, int32_t B, int32_t H, int32_
     return NABLA_OK;
 }
 
+nabla_status_t nabla_check_lists(const int32_t* count, const int32_t* idx, int32_t B, int32_t H,
+                                 int32_t S, int32_t N, int32_t* bad_rows, void* stream) {
+    Shape s;
+    const nabla_status_t st = check_shape(B, H, S, kStaShapeD, N, &s);
+    if (st != NABLA_OK) return st;
+    if (!count || !idx || !bad_rows) return NABLA_ERR_INVALID_ARG;
+    NABLA_LAUNCH(launch_check_lists(count, idx, s.BH * s.n, (int)s.n, bad_rows, as_stream(stream)));
+    return NABLA_OK;
+}
+
 nabla_status_t nabla_reorder_tokens(const void* src, void* dst, int32_t B, int32_t T, int32_t Hs,
                                     int32_t Ws, int32_t P, int64_t row_bytes, int32_t inverse,
                                     void* stream) {

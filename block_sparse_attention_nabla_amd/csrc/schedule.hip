@@ -82,6 +82,46 @@ hipError_t launch_lpt_order(const int32_t* counts, int64_t BH, int items, int ma
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(64) void zero_count_kernel(int32_t* __restrict__ bad) {
+    if (threadIdx.x == 0) *bad = 0;
+}
+
+// One wave per row: the count in [0, n]; the first `count` entries in [0, n)
+// and strictly ascending (each lane compares its entry with the previous
+// lane's, lane 0 with the last entry of the previous 64).
+__global__ __launch_bounds__(256) void check_lists_kernel(const int32_t* __restrict__ count,
+                                                          const int32_t* __restrict__ idx,
+                                                          int64_t rows, int n,
+                                                          int32_t* __restrict__ bad) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;  // whole wave
+    const int c = count[row];
+    bool ok = c >= 0 && c <= n;
+    if (ok) {
+        const int32_t* l = idx + row * (int64_t)n;
+        int prev_last = -1;
+        for (int base = 0; base < c && ok; base += 64) {
+            const int i = base + lane;
+            const int v = i < c ? l[i] : 0;
+            const int up = __shfl_up(v, 1);
+            const int prev = lane == 0 ? prev_last : up;
+            const bool wrong = i < c && (v < 0 || v >= n || (i > 0 && v <= prev));
+            if (__ballot(wrong)) ok = false;
+            prev_last = __shfl(v, 63);
+        }
+    }
+    if (!ok && lane == 0) atomicAdd(bad, 1);
+}
+
+hipError_t launch_check_lists(const int32_t* count, const int32_t* idx, int64_t rows, int n,
+                              int32_t* bad, hipStream_t stream) {
+    zero_count_kernel<<<1, 64, 0, stream>>>(bad);
+    if (rows > 0)
+        check_lists_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(count, idx, rows, n, bad);
+    return hipGetLastError();
+}
+
 XcdSchedule make_schedule(int64_t BH, int n) {
     int64_t a = BH, b = 8;  // gcd(BH, 8)
     while (b != 0) {

@@ -241,6 +241,26 @@ NABLA_API nabla_status_t nabla_mask_recall(const float* mass, int32_t B, int32_t
                                            float* recall, float* best_recall, void* stream);
 
 /*
+ * Block-list check. The attention and diagnostic kernels read lists defensively:
+ * a count outside [0, n] is clamped into it and an entry outside [0, n) is read
+ * as block 0, so a malformed list gives wrong results rather than an error (and
+ * a non-ascending list is processed in its own order). Callers that build or
+ * edit lists themselves can check them first: this counts the rows (b, h, i)
+ * whose list is malformed -- kv_count outside [0, n], or among the first
+ * kv_count entries one outside [0, n) or one not larger than its predecessor
+ * (the lists every nabla_build_*_mask writes, kv and q lists alike, are
+ * strictly ascending and pass) -- and writes the number to *bad_rows (one
+ * device int32, overwritten, written by the GPU: read it after the stream has
+ * reached this call). count: int32 [B, H, n]; idx: int32 [B, H, n, n], row
+ * stride n; n = S / N with S % N == 0 and N == 64 as for the other calls.
+ * NABLA_ERR_INVALID_ARG for null pointers. No workspace; enqueued on `stream`
+ * like every call.
+ */
+NABLA_API nabla_status_t nabla_check_lists(const int32_t* count, const int32_t* idx, int32_t B,
+                                           int32_t H, int32_t S, int32_t N, int32_t* bad_rows,
+                                           void* stream);
+
+/*
  * Token reordering, section 3.1.1 (Figure 3): "fractal flattening", applied to
  * the token sequence at the input of the network, and its inverse at the output.
  * Each of the B items holds T frames of Hs x Ws tokens; raster order is

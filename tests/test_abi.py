@@ -232,3 +232,12 @@ def test_static_forward_rejects_shapes_beyond_its_scratch(lib):
     assert st == WORKSPACE
     st = lib.nabla_sparse_attn_fwd_static(p, p, p, 1, 1, 100, 64, 64, p, p, 0.125, 0, p, 0, None, None)
     assert st == INVALID  # S % N != 0
+
+
+def test_check_lists_validation(lib):
+    cl = lib.nabla_check_lists
+    assert cl(P, P, 1, 2, 1000, 64, P, None) == INVALID   # S % N
+    assert cl(None, P, 1, 2, 1024, 64, P, None) == INVALID
+    assert cl(P, None, 1, 2, 1024, 64, P, None) == INVALID
+    assert cl(P, P, 1, 2, 1024, 64, None, None) == INVALID
+    assert cl(P, P, 1, 2, 1024, 32, P, None) == UNSUPPORTED

@@ -106,3 +106,12 @@ def test_diagnostic_and_reorder_arguments():
     x = torch.zeros((1, 4 * 16 * 16, 32), dtype=torch.bfloat16)
     _raises("out has shape", nb.nabla_reorder_tokens, x, 4, 16, 16, 8, out=x[:, :-1].contiguous())
     _raises("HIP", nb.nabla_reorder_tokens, x, 4, 16, 16, 8)
+
+
+def test_check_lists_arguments():
+    cnt, idx = _lists()
+    _raises("count must be", nb.nabla_check_lists, cnt.reshape(-1), idx)
+    _raises("count has dtype", nb.nabla_check_lists, cnt.long(), idx)
+    _raises("idx has shape", nb.nabla_check_lists, cnt, idx[..., :1].contiguous())
+    _raises("idx has dtype", nb.nabla_check_lists, cnt, idx.float())
+    _raises("CUDA", nb.nabla_check_lists, cnt, idx)

@@ -32,6 +32,10 @@
 //                         K/V tile once, and each pair of waves computes only
 //                         the blocks of its own list -- in the same order as
 //                         the single kernel, so the results are bitwise equal.
+//                         For D = 128 it moves its tiles by direct-to-LDS
+//                         loads into swizzled unpadded rows (see its
+//                         specialization below); D = 64 stages them through
+//                         registers like the single kernel.
 // The forward is bound by K/V tile traffic from beyond L2 (each kept pair
 // reads a 32 KB tile pair); sharing tiles between the two blocks of a pair
 // removes the loads of their common blocks.
@@ -467,6 +471,246 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
 
 #undef NABLA_PFETCH
 #undef NABLA_PSTAGE
+    if (active) store_rows<D>(st, head, qrow, h, o, o_fp32, lse, bh * (int64_t)S + qrow);
+}
+
+// ---------------------------------------------------------------------------
+// attn_fwd_pair_kernel for D = 128: the same walk and block step as the
+// generic pair kernel, but the K/V tiles move global -> LDS by direct-to-LDS
+// loads (global_load_lds_dwordx4: each wave instruction fills 1 KB = four
+// 256-byte tile rows), with no staging registers and no LDS stores in the
+// waves' instruction streams. Tile rows are unpadded; the 16-byte chunk ch of
+// row r is stored at ch ^ (r % 16) in the K tile and at ch ^ 4 (r % 4) in the
+// V tile, which keeps the K row reads (ds_read_b128, 16 consecutive rows) and
+// the V transposing reads (ds_read_b64_tr_b16, four chunks of four
+// consecutive rows) free of bank conflicts; each lane's read addresses are
+// computed once (XOR patterns). The next union step's tiles are requested
+// into the other buffer at the start of a step and waited for at its end (one
+// barrier per step). The two buffers are separate arrays and the loop is
+// unrolled by two, so every LDS access names its buffer statically and the
+// compiler's wait counting never makes a read wait for loads into the other
+// buffer. Same operations in the same order as attn_fwd_kernel: bitwise equal.
+// ---------------------------------------------------------------------------
+namespace {
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+// s_waitcnt vmcnt(0), other counters unconstrained.
+__device__ __forceinline__ void dma_wait_all() {
+    __builtin_amdgcn_s_waitcnt((0 & 15) | ((0 >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier that waits for this wave's LDS accesses (lgkmcnt 0) but
+// not for direct-to-LDS loads in flight (the caller waits for those), and that
+// no memory access crosses.
+__device__ __forceinline__ void dma_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// A workgroup-uniform pointer kept in scalar registers and opaque to the
+// optimiser, so a 32-bit lane offset added to it selects the scalar-base +
+// vector-offset address form.
+__device__ __forceinline__ const char* uniform_cptr(const char* p) {
+    uint64_t x = reinterpret_cast<uint64_t>(p);
+    asm volatile("" : "+s"(x));
+    return reinterpret_cast<const char*>(x);
+}
+// Mark a value as produced here: keeps a 32-bit offset from being folded into
+// a hoisted 64-bit pointer, and keeps loop-invariant loads from being waited
+// for inside the loop.
+template <typename T_>
+__device__ __forceinline__ void settle_v(T_& x) { asm volatile("" : "+v"(x)); }
+
+// One kept block from swizzled tiles: K row reads at kl[kk] (+ 8192 for the
+// second 32-key tile), V transposing reads at vl[t] (+ row offsets).
+__device__ __forceinline__ void block_step_swz(RowState<128>& st, const char* kt0, const char* vt0,
+                                               const uint32_t (&kl)[8], const uint32_t (&vl)[4],
+                                               float scale_log2) {
+    constexpr int KK = 8, DT = 4;
+    const uint32_t ones_bf16x2 = 0x3f803f80u;
+    __builtin_amdgcn_s_setprio(1);
+    f32x16_t s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        bf16x8_t a[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kt0 + 8192 * kt + kl[kk]));
+        s[kt] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s[kt] = mfma_32x32x16(a[kk], st.qf[kk], s[kt]);
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[1][r]);
+    mx = pair_max(mx) * scale_log2;
+    const bool grow = mx > st.m_run + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : st.m_run;
+        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+        st.l_run *= alpha;
+        st.w_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[t][r] *= alpha;
+        st.m_run = m_new;
+    }
+    float rs = 0.f, ws = 0.f;
+    uint32_t pw[2][8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(s[kt][2 * e] * scale_log2 - st.m_run);
+            const float p1 = __builtin_amdgcn_exp2f(s[kt][2 * e + 1] * scale_log2 - st.m_run);
+            rs += p0 + p1;
+            pw[kt][e] = pack_bf16x2(p0, p1);
+            ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[kt][e]),
+                                                 __builtin_bit_cast(bf16x2_t, ones_bf16x2), ws, false);
+        }
+    st.l_run += rs;
+    st.w_run += ws;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8_t b = as_bf16x8(make_uint4(pw[kt][4 * u], pw[kt][4 * u + 1],
+                                                    pw[kt][4 * u + 2], pw[kt][4 * u + 3]));
+            const char* vrow = vt0 + (32 * kt + 16 * u) * 256;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vrow + vl[t]));
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vrow + 8 * 256 + vl[t]));
+                const uint2 ulo = __builtin_bit_cast(uint2, lo);
+                const uint2 uhi = __builtin_bit_cast(uint2, hi);
+                st.oacc[t] = mfma_32x32x16(as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y)), b, st.oacc[t]);
+            }
+        }
+    __builtin_amdgcn_s_setprio(0);
+}
+}  // namespace
+
+template <>
+__global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel<128>(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int S, int n, int F, const int32_t* __restrict__ kv_count,
+    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ order, XcdSchedule sched,
+    float scale_log2, void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
+    constexpr int D = 128;
+    constexpr int TB = kBlockN * 2 * D;  // 16 KB per tile
+    __shared__ __attribute__((aligned(1024))) char sK0[TB];
+    __shared__ __attribute__((aligned(1024))) char sV0[TB];
+    __shared__ __attribute__((aligned(1024))) char sK1[TB];
+    __shared__ __attribute__((aligned(1024))) char sV1[TB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 1;
+    const int h = lane >> 5, c = lane & 31;
+    const int64_t pair = scheduled_item(sched, order, blockIdx.x);
+    if (pair < 0) return;
+    const int np = sched.n;
+    const int64_t bh = pair / np;
+    const int p = (int)(pair % np);
+    const int s2 = 2 * (p / F), tp = p % F;
+    const int qa = s2 * F + tp;
+    const int qbB = qa + F < n ? qa + F : -1;
+    const int64_t itemA = bh * (int64_t)n + qa;
+    const int64_t itemB = bh * (int64_t)n + (qbB < 0 ? qa : qbB);
+    int cntA = kv_count[itemA];
+    cntA = cntA < 0 ? 0 : (cntA > n ? n : cntA);
+    int cntB = qbB < 0 ? 0 : kv_count[itemB];
+    cntB = cntB < 0 ? 0 : (cntB > n ? n : cntB);
+    const int32_t* listA = kv_idx + itemA * (int64_t)n;
+    const int32_t* listB = kv_idx + itemB * (int64_t)n;
+    const int64_t head = bh * (int64_t)S * D;
+    const char* kh = reinterpret_cast<const char*>(k + head);
+    const char* vh = reinterpret_cast<const char*>(v + head);
+
+    const int my_qb = grp ? qbB : qa;
+    const bool active = my_qb >= 0;
+    const int64_t qrow = (int64_t)(active ? my_qb : qa) * kBlockN + (wave & 1) * 32 + c;
+    RowState<D> st;
+    load_rows<D>(st, q + head + qrow * D, h);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) settle_v(st.qf[kk]);
+
+    // Read addresses (bytes within a tile).
+    uint32_t kl[8], vl[4];
+    {
+        const int x = c & 15;
+        const uint32_t kb = (uint32_t)(c * 256 + 16 * (h ^ (x & 1)) + 32 * (x >> 1));
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) kl[kk] = kb ^ (32u * kk);
+        const int y = (lane & 15) >> 2, g = (lane >> 4) & 1;
+        const uint32_t vb = (uint32_t)((4 * h + y) * 256 + 16 * (2 * g + ((lane & 3) >> 1)) + 8 * (lane & 1) + 64 * y);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vl[t] = vb ^ (64u * t);
+    }
+    // Direct-to-LDS loads: wave w fills row groups m = w + 4 i (rows 4m .. 4m + 3);
+    // lane L writes physical chunk L % 16 of row 4m + L / 16 and fetches the
+    // logical chunk stored there.
+    uint32_t gk, gv;
+    {
+        const int r = 4 * wave + (lane >> 4);
+        gk = (uint32_t)(r * 256 + 16 * ((lane & 15) ^ (r & 15)));
+        gv = (uint32_t)(r * 256 + 16 * ((lane & 15) ^ (4 * (r & 3))));
+    }
+    auto dma = [&](int j, char* dk_, char* dv_) {
+        const char* ks = uniform_cptr(kh + (int64_t)j * TB);
+        const char* vs = uniform_cptr(vh + (int64_t)j * TB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t ok = gk + 4096u * i, ov = gv + 4096u * i;
+            settle_v(ok);
+            settle_v(ov);
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(ks + ok), (lds_void_t*)(dk_ + 1024 * (wave + 4 * i)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(vs + ov), (lds_void_t*)(dv_ + 1024 * (wave + 4 * i)), 16, 0, 0);
+        }
+    };
+    // Union cursor (workgroup-uniform).
+    int ia = 0, ib = 0;
+    auto adv = [&](int& j, int& flags) {
+        const int ja0 = ia < cntA ? __builtin_amdgcn_readfirstlane(listA[ia]) : n;
+        const int jb0 = ib < cntB ? __builtin_amdgcn_readfirstlane(listB[ib]) : n;
+        const int ja = (unsigned)ja0 <= (unsigned)n ? ja0 : 0;
+        const int jb = (unsigned)jb0 <= (unsigned)n ? jb0 : 0;
+        j = ja < jb ? ja : jb;
+        flags = j >= n ? 0 : ((ja == j ? 1 : 0) | (jb == j ? 2 : 0));
+        ia += flags & 1;
+        ib += (flags >> 1) & 1;
+    };
+    int j_cur, f_cur, j_nxt, f_nxt;
+    adv(j_cur, f_cur);
+    if (f_cur) {
+        dma(j_cur, sK0, sV0);
+        adv(j_nxt, f_nxt);
+        dma_wait_all();
+        dma_barrier();
+        // One step: load the next step's tiles into the other buffer, compute
+        // this step from its buffer, advance, wait, meet.
+        auto one = [&](const char* ck, const char* cv, char* nk, char* nv) {
+            // Next step's tiles; with no next step, any valid block (never read).
+            dma(f_nxt ? j_nxt : (f_cur ? j_cur : 0), nk, nv);
+            const int mine = grp ? (f_cur & 2) : (f_cur & 1);
+            if (mine && active) block_step_swz(st, ck, cv, kl, vl, scale_log2);
+            j_cur = j_nxt;
+            f_cur = f_nxt;
+            if (f_cur) adv(j_nxt, f_nxt);
+            else f_nxt = 0;
+            dma_wait_all();
+            dma_barrier();
+        };
+        for (;;) {
+            one(sK0, sV0, sK1, sV1);
+            one(sK1, sV1, sK0, sV0);
+            if (f_cur == 0) break;
+        }
+    }
     if (active) store_rows<D>(st, head, qrow, h, o, o_fp32, lse, bh * (int64_t)S + qrow);
 }
 

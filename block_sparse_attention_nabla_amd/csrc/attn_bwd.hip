@@ -333,7 +333,8 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
 // LDS, B = Q^T / dO^T in registers; accumulator rows = keys), then
 // dQ^T += K_j^T dS^T over its 32 keys (A = transposed reads of the K_j tile).
 // The two waves of a query half sum their partial dQ once, through LDS, at
-// the end. Small per-wave state (about 220 registers) lets two workgroups --
+// the end (D = 128 moves its tiles by direct-to-LDS loads: see its
+// specialization below). Small per-wave state (about 220 registers) lets two workgroups --
 // two waves per SIMD -- share a CU, so one wave's products overlap the other's
 // softmax and LDS reads.
 // ---------------------------------------------------------------------------
@@ -460,6 +461,219 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
     // register order (lane-contiguous words), the kh = 0 wave adds and stores.
     __syncthreads();  // tiles no longer read
     float* red = reinterpret_cast<float*>(sKV) + qh * (DT * 16 * kWave);
+    if (kh == 1) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(t * 16 + r) * kWave + lane] = dQt[t][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dQt[t][r] += red[(t * 16 + r) * kWave + lane];
+        store_t_acc<DT>(dq + head + (int64_t)qrow * D, dQt, scale, h);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq_kernel for D = 128: the same quadrant split and operations in the same
+// order (bitwise equal results), but the K/V tiles move global -> LDS by
+// direct-to-LDS loads (global_load_lds_dwordx4, 1 KB = four unpadded 256-byte
+// rows per wave instruction) into two buffers: the next key block's tiles are
+// requested at the start of a step and waited for at its end (one barrier per
+// step), with no staging registers and no LDS stores in the waves' streams.
+// Unpadded rows are swizzled per 16-byte chunk: K, read both row-wise and
+// transposed, keeps chunk ch of row r at ch ^ (4 (r % 4) + (r / 4) % 4); V,
+// read row-wise only, at ch ^ (r % 16); both read kinds are then free of bank
+// conflicts, and each lane's 24 read addresses are computed once. The two
+// buffers are separate arrays and the loop is unrolled by two with a
+// branch-free step, so no LDS read waits for loads into the other buffer.
+// ---------------------------------------------------------------------------
+namespace {
+typedef __attribute__((address_space(3))) void bwd_lds_void_t;
+typedef __attribute__((address_space(1))) const void bwd_gbl_void_t;
+// s_waitcnt vmcnt(0), other counters unconstrained.
+__device__ __forceinline__ void bwd_wait_vm0() {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+// Workgroup barrier that waits for this wave's LDS accesses (lgkmcnt 0) but not
+// for direct-to-LDS loads in flight, and that no memory access crosses.
+__device__ __forceinline__ void bwd_tile_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// A workgroup-uniform pointer kept in scalar registers and opaque to the
+// optimiser (scalar-base + 32-bit vector-offset loads).
+__device__ __forceinline__ const char* bwd_uniform_ptr(const char* p) {
+    uint64_t x = reinterpret_cast<uint64_t>(p);
+    asm volatile("" : "+s"(x));
+    return reinterpret_cast<const char*>(x);
+}
+// Swizzles of unpadded 256-byte rows (16 chunks of 16 B): chunk ch of row r at
+// ch ^ swz(r). K is read row-wise and transposed: 4 (r % 4) + (r / 4) % 4 keeps
+// both conflict-free; V is read row-wise only: r % 16.
+__device__ __forceinline__ int swz_k(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz_v(int r) { return r & 15; }
+}  // namespace
+
+template <>
+__global__ __launch_bounds__(256, 2) void dq_kernel<128>(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
+    const float* __restrict__ lse, const float* __restrict__ delta, int S, int n,
+    const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_idx,
+    const int32_t* __restrict__ order, XcdSchedule sched, float scale, float scale_log2,
+    uint16_t* __restrict__ dq) {
+    constexpr int D = 128, KK = 8, DT = 4;
+    constexpr int TB = kBlockN * 2 * D;  // 16 KB
+    __shared__ __attribute__((aligned(1024))) char sK0[TB];
+    __shared__ __attribute__((aligned(1024))) char sV0[TB];
+    __shared__ __attribute__((aligned(1024))) char sK1[TB];
+    __shared__ __attribute__((aligned(1024))) char sV1[TB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, c = lane & 31;
+    const int kh = wave & 1, qh = wave >> 1;
+    const int64_t item = scheduled_item(sched, order, blockIdx.x);
+    if (item < 0) return;
+    const int64_t bh = item / n;
+    const int qb = (int)(item % n);
+    int cnt = kv_count[item];
+    cnt = cnt < 0 ? 0 : (cnt > n ? n : cnt);
+    const int32_t* list = kv_idx + item * (int64_t)n;
+    const int64_t head = bh * (int64_t)S * D;
+    const char* khp = reinterpret_cast<const char*>(k + head);
+    const char* vhp = reinterpret_cast<const char*>(v + head);
+
+    const int qrow = qb * kBlockN + qh * 32 + c;
+    bf16x8_t qf[KK], dof[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        qf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(q + head + (int64_t)qrow * D + 16 * kk + 8 * h));
+        dof[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(d_o + head + (int64_t)qrow * D + 16 * kk + 8 * h));
+    }
+    float l2 = lse[bh * (int64_t)S + qrow] * kLog2e;
+    float del = delta[bh * (int64_t)S + qrow];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        settle(qf[kk]);
+        settle(dof[kk]);
+    }
+    settle(l2);
+    settle(del);
+    f32x16_t dQt[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) dQt[t] = zero16();
+
+    // Read addresses within a tile.
+    uint32_t ka[KK], va[KK], ta[2][DT];
+    {
+        const int x = c & 15;
+        const int row = 32 * kh + c;
+        const uint32_t kb = (uint32_t)(row * 256 + 16 * ((h ^ (swz_k(x) & 1)) + 2 * (swz_k(x) >> 1)));
+        const uint32_t vb = (uint32_t)(row * 256 + 16 * ((h ^ (swz_v(x) & 1)) + 2 * (swz_v(x) >> 1)));
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            ka[kk] = kb ^ (32u * kk);
+            va[kk] = vb ^ (32u * kk);
+        }
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+            const int xr = 8 * hi + 4 * (lane >> 5) + ((lane & 15) >> 2);
+            const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            const uint32_t tb = (uint32_t)(xr * 256 + 16 * (c0 ^ swz_k(xr)) + 8 * (lane & 1));
+#pragma unroll
+            for (int t = 0; t < DT; ++t) ta[hi][t] = tb ^ (64u * t);
+        }
+    }
+    // Direct-to-LDS loads: wave w fills row groups m = w + 4 i.
+    uint32_t gk, gv;
+    {
+        const int r0 = 4 * wave + (lane >> 4);
+        gk = (uint32_t)(r0 * 256 + 16 * ((lane & 15) ^ swz_k(r0)));
+        gv = (uint32_t)(r0 * 256 + 16 * ((lane & 15) ^ swz_v(r0)));
+    }
+    auto entry = [&](int i) {
+        const int b = __builtin_amdgcn_readfirstlane(list[i]);
+        return (unsigned)b < (unsigned)n ? b : 0;
+    };
+    auto fetch = [&](int j, char* dk_, char* dv_) {
+        const char* ks = bwd_uniform_ptr(khp + (int64_t)j * TB);
+        const char* vs = bwd_uniform_ptr(vhp + (int64_t)j * TB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t ok = gk + 4096u * i, ov = gv + 4096u * i;
+            settle(ok);
+            settle(ov);
+            __builtin_amdgcn_global_load_lds((bwd_gbl_void_t*)(ks + ok), (bwd_lds_void_t*)(dk_ + 1024 * (wave + 4 * i)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((bwd_gbl_void_t*)(vs + ov), (bwd_lds_void_t*)(dv_ + 1024 * (wave + 4 * i)), 16, 0, 0);
+        }
+    };
+    auto compute = [&](const char* sK, const char* sV) {
+        uint32_t dsw[8];
+        {
+            f32x16_t sc = zero16(), dp = zero16();
+            {
+                bf16x8_t a[KK];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(sK + ka[kk]));
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) sc = mfma_32x32x16(a[kk], qf[kk], sc);
+            }
+            {
+                bf16x8_t a[KK];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(sV + va[kk]));
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) dp = mfma_32x32x16(a[kk], dof[kk], dp);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(sc[r] * scale_log2 - l2);
+                dp[r] = p * (dp[r] - del);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dsw[e] = pack_bf16x2(dp[2 * e], dp[2 * e + 1]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8_t bs = as_bf16x8(make_uint4(dsw[4 * u], dsw[4 * u + 1], dsw[4 * u + 2], dsw[4 * u + 3]));
+            const char* rb = sK + (32 * kh + 16 * u) * 256;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(rb + ta[0][t]));
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(rb + ta[1][t]));
+                const uint2 ulo = __builtin_bit_cast(uint2, lo);
+                const uint2 uhi = __builtin_bit_cast(uint2, hi);
+                dQt[t] = mfma_32x32x16(as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y)), bs, dQt[t]);
+            }
+        }
+    };
+    auto step = [&](int it, const char* cK, const char* cV, char* nK, char* nV) {
+        fetch(entry(min(it + 1, cnt - 1)), nK, nV);
+        compute(cK, cV);
+        bwd_wait_vm0();
+        bwd_tile_barrier();
+    };
+    if (cnt > 0) {
+        fetch(entry(0), sK0, sV0);
+        bwd_wait_vm0();
+        bwd_tile_barrier();
+        int it = 0;
+        for (; it + 1 < cnt; it += 2) {
+            step(it, sK0, sV0, sK1, sV1);
+            step(it + 1, sK1, sV1, sK0, sV0);
+        }
+        if (it < cnt) step(it, sK0, sV0, sK1, sV1);
+    }
+    // Sum the two key halves through LDS (tiles no longer read).
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(qh ? sV0 : sK0);
     if (kh == 1) {
 #pragma unroll
         for (int t = 0; t < DT; ++t)

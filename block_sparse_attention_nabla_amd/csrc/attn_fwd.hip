@@ -529,16 +529,29 @@ __device__ __forceinline__ void block_step_swz(RowState<128>& st, const char* kt
     constexpr int KK = 8, DT = 4;
     const uint32_t ones_bf16x2 = 0x3f803f80u;
     __builtin_amdgcn_s_setprio(1);
+    // S^T: all of key tile 0's K fragments read first, then tile 1's reads
+    // interleaved with tile 0's products (order pinned with scheduling groups).
     f32x16_t s[2];
+    {
+        bf16x8_t a0[KK], a1[KK];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        bf16x8_t a[KK];
+        for (int kk = 0; kk < KK; ++kk) a0[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kt0 + kl[kk]));
+        s[0] = zero16();
+        s[1] = zero16();
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kt0 + 8192 * kt + kl[kk]));
-        s[kt] = zero16();
+        for (int kk = 0; kk < KK; ++kk) {
+            a1[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kt0 + 8192 + kl[kk]));
+            s[0] = mfma_32x32x16(a0[kk], st.qf[kk], s[0]);
+        }
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s[kt] = mfma_32x32x16(a[kk], st.qf[kk], s[kt]);
+        for (int kk = 0; kk < KK; ++kk) s[1] = mfma_32x32x16(a1[kk], st.qf[kk], s[1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, KK, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, KK, 0);
     }
     float mx = s[0][0];
 #pragma unroll

@@ -77,26 +77,35 @@ nabla_status_t content_mask(int mode, int keep_all, uint64_t bound, const void* 
 
     const float scale = 1.0f / sqrtf((float)s.D);
     NABLA_LAUNCH(launch_pool(q, k, po, s.BH, (int)s.n, (int)s.D, hs));
-    NABLA_LAUNCH(launch_logits(po.qa, po.ka, logits, s.BH, (int)s.n, (int)s.D, scale, hs));
-    SelectArgs a{};
-    a.logits = logits;
-    a.rows = s.BH * s.n;
-    a.n = (int)s.n;
-    a.keep_all = keep_all;
-    a.bound = bound;
-    a.sta = sta_params(sta);
-    a.qa64 = po.qa64;
-    a.ka64 = po.ka64;
-    a.qnorm = po.qnorm;
-    a.kmax = po.kmax;
-    a.scale64 = 1.0 / sqrt((double)s.D);
-    a.err_unit = logit_error_unit((int)s.D, scale);
-    a.kv_count = kv_count;
-    a.kv_idx = kv_idx;
-    a.dense_mask = dense_mask;
-    a.bits = bits;
-    a.words_per_row = w.words_per_row;
-    NABLA_LAUNCH(launch_select(mode, a, (int)s.D, hs));
+    // Reduced logits and selection, w.logit_heads heads at a time (the map
+    // region holds that many heads; one chunk unless B*H*n*n*4 bytes exceed
+    // kMaxLogitMapBytes). Every per-row and per-head array is offset to the
+    // chunk's first head; the kernels index them from there.
+    const int64_t n = s.n, dim = s.D;
+    for (int64_t h0 = 0; h0 < s.BH; h0 += w.logit_heads) {
+        const int64_t nh = s.BH - h0 < w.logit_heads ? s.BH - h0 : w.logit_heads;
+        const int64_t r0 = h0 * n;  // first row of the chunk
+        NABLA_LAUNCH(launch_logits(po.qa + r0 * dim, po.ka + r0 * dim, logits, nh, (int)n, (int)dim, scale, hs));
+        SelectArgs a{};
+        a.logits = logits;
+        a.rows = nh * n;
+        a.n = (int)n;
+        a.keep_all = keep_all;
+        a.bound = bound;
+        a.sta = sta_params(sta);
+        a.qa64 = po.qa64 + r0 * dim;
+        a.ka64 = po.ka64 + r0 * dim;
+        a.qnorm = po.qnorm + r0;
+        a.kmax = po.kmax + h0;
+        a.scale64 = 1.0 / sqrt((double)s.D);
+        a.err_unit = logit_error_unit((int)s.D, scale);
+        a.kv_count = kv_count + r0;
+        a.kv_idx = kv_idx + r0 * n;
+        a.dense_mask = dense_mask ? dense_mask + r0 * n : nullptr;
+        a.bits = bits ? bits + r0 * w.words_per_row : nullptr;
+        a.words_per_row = w.words_per_row;
+        NABLA_LAUNCH(launch_select(mode, a, (int)s.D, hs));
+    }
     if (q_idx)
         NABLA_LAUNCH(launch_transpose(bits, s.BH, (int)s.n, w.words_per_row, q_count, q_idx, hs));
     return NABLA_OK;

@@ -47,7 +47,10 @@ MaskWorkspace mask_workspace(const Shape& s) {
     w.knorm = w.qnorm + align256(norms);
     w.kmax = w.knorm + align256(norms);
     w.logits = w.kmax + align256((size_t)s.BH * sizeof(float));
-    w.bits = w.logits + align256((size_t)s.BH * s.n * s.n * sizeof(float));
+    const size_t head_map = (size_t)s.n * s.n * sizeof(float);
+    int64_t heads = (int64_t)(kMaxLogitMapBytes / head_map);
+    w.logit_heads = heads < 1 ? 1 : (heads > s.BH ? s.BH : heads);
+    w.bits = w.logits + align256((size_t)w.logit_heads * head_map);
     w.total = w.bits + align256((size_t)s.BH * s.n * w.words_per_row * sizeof(uint32_t));
     return w;
 }

@@ -14,8 +14,14 @@ struct Shape {
 };
 
 // Region offsets inside a caller-provided workspace (all 256-byte aligned).
+// The reduced-logit map is held for `logit_heads` heads at a time: as many as
+// fit kMaxLogitMapBytes (at least one), so the workspace grows with one head's
+// n x n map instead of all B*H of them; the mask call walks the heads in
+// chunks of that many.
+constexpr size_t kMaxLogitMapBytes = (size_t)256 << 20;
 struct MaskWorkspace {
     size_t qa, ka, qa64, ka64, qnorm, knorm, kmax, logits, bits, total;
+    int64_t logit_heads;
     int words_per_row;
 };
 struct StaWorkspace {

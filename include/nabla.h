@@ -73,7 +73,10 @@ enum { NABLA_OP_MASK = 0, NABLA_OP_FWD = 1, NABLA_OP_BWD = 2, NABLA_OP_STA_MASK 
 /* Element type of the forward output O. */
 enum { NABLA_DTYPE_BF16 = 0, NABLA_DTYPE_FP32 = 1 };
 
-/* Bytes of device workspace the given operation needs (0 for invalid shapes). */
+/* Bytes of device workspace the given operation needs (0 for invalid shapes).
+ * NABLA_OP_MASK is linear in B*H*n except for the fp32 reduced-logit map,
+ * which the mask call keeps for a chunk of heads at a time: as many heads as
+ * fit 256 MiB of n x n maps, at least one (n = S/N). */
 NABLA_API size_t nabla_workspace_size(int32_t op, int32_t B, int32_t H, int32_t S, int32_t D, int32_t N);
 
 /* Human-readable name of a status code (static storage). */

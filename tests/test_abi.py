@@ -58,6 +58,29 @@ def test_workspace_sizes(lib):
     assert nb.nabla_workspace_size(7, B, H, S, D) == 0
 
 
+def test_mask_workspace_holds_the_logit_map_for_a_chunk_of_heads(lib):
+    # Linear terms per head row: fp32 + fp64 means of Q and K, two norms; plus
+    # bitmask words. The n x n fp32 map is held for as many heads as fit
+    # 256 MiB, at least one.
+    def linear(B, H, S, D):
+        n = S // 64
+        return B * H * n * (2 * D * 4 + 2 * D * 8 + 2 * 4 + ((n + 31) // 32) * 4)
+
+    cap = 256 << 20
+    for B, H, S, D in [(1, 40, 80640, 128), (2, 16, 61440, 128), (1, 2, 64 * 6144, 64),
+                       (1, 40, 64 * 8192, 128)]:
+        n = S // 64
+        head_map = n * n * 4
+        heads = max(1, min(B * H, cap // head_map))
+        size = nb.nabla_workspace_size(nb.NABLA_OP_MASK, B, H, S, D)
+        want = linear(B, H, S, D) + heads * head_map
+        assert want <= size <= want + 16 * 256 + B * H * 4, (B, H, S, D, size, want)
+    # 720p (40 heads, n = 1260) keeps its whole map in one chunk; n = 8192 with
+    # 40 heads needs one head's map (268 MB), not all forty (10.7 GB).
+    assert nb.nabla_workspace_size(nb.NABLA_OP_MASK, 1, 40, 80640, 128) > 40 * 1260 * 1260 * 4
+    assert nb.nabla_workspace_size(nb.NABLA_OP_MASK, 1, 40, 64 * 8192, 128) < 2 * 8192 * 8192 * 4 + (2 << 30)
+
+
 # Fake, 256-aligned, never-dereferenced device addresses: every call below
 # fails validation before anything touches them.
 P = ctypes.c_void_p(0x7F0000000000)

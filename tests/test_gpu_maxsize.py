@@ -119,6 +119,45 @@ def test_max_blocks_mask_forward_backward():
     print(f"[max] bwd sampled {res}", flush=True)
 
 
+def test_mask_map_in_head_chunks():
+    """Two heads at n = 6144: one head's reduced map (151 MB) fills the library's
+    256 MiB map region alone, so the mask call computes the logits and the
+    selection once per head, each into the same region. Both heads' lists must
+    follow the CDF rule on the oracle's fp64 map (outside the 1e-5 band), and equal
+    what one-head calls on the same data give."""
+    nb = _nb()
+    n, D, thr, H = 6144, 64, 0.3, 2
+    S = 64 * n
+    head_map = n * n * 4
+    assert 2 * head_map > (256 << 20) >= head_map  # one head per chunk
+    assert nb.nabla_workspace_size(nb.NABLA_OP_MASK, 1, H, S, D) < H * head_map
+    per_head = [_inputs(S, D, seed=91 + h) for h in range(H)]
+    q = torch.cat([t[0] for t in per_head], dim=1)  # [1, H, S, D]
+    k = torch.cat([t[1] for t in per_head], dim=1)
+    qg, kg = q.cuda(), k.cuda()
+    print(f"[chunks] n={n} H={H} D={D} thr={thr}", flush=True)
+    out = nb.nabla_build_mask(qg, kg, thr, transpose=True, dense=True)
+    torch.cuda.synchronize()
+    cnt = out["kv_count"].cpu().numpy()
+    dense = out["dense_mask"].cpu().numpy().reshape(H, n, n)
+    np.testing.assert_array_equal(lists_to_mask(cnt, out["kv_idx"].cpu().numpy()), dense)
+    np.testing.assert_array_equal(
+        lists_to_mask(out["q_count"].cpu().numpy(), out["q_idx"].cpu().numpy()), np.swapaxes(dense, 1, 2))
+    qa = oracle.pool(q.float().reshape(H, S, D), 64)
+    ka = oracle.pool(k.float().reshape(H, S, D), 64)
+    p = oracle.reduced_map(qa, ka, 1.0 / np.sqrt(D))
+    for h in range(H):
+        res = _check_cdf_rows(p[h], dense[h].astype(bool), thr)
+        print(f"[chunks] head {h}: kept {int(cnt[0, h].sum())}, CDF rule check {res}", flush=True)
+        assert res["unexplained"] == 0, (h, res)
+    del p
+    for h in range(H):
+        one = nb.nabla_build_mask(qg[:, h:h + 1].contiguous(), kg[:, h:h + 1].contiguous(), thr)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(
+            lists_to_mask(one["kv_count"].cpu().numpy(), one["kv_idx"].cpu().numpy())[0], dense[h])
+
+
 def test_rows_beyond_the_maximum_are_rejected():
     nb = _nb()
     S = 64 * (N_MAX + 1)

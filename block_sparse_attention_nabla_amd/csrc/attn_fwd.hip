@@ -17,7 +17,10 @@
 // reads (the pair kernel below double-buffers them), so global latency
 // overlaps a whole block of compute. exp2 is used
 // with log2(e) folded into the scale, and the output is rescaled only when a
-// row maximum grows by more than 2^8. A wave raises its issue priority for the
+// row maximum grows by more than 2^8; the block maximum is formed only when
+// the exponentials taken against the running maximum could have reached that
+// (softmax_lazy), which leaves every result unchanged and keeps the max
+// reduction out of most steps. A wave raises its issue priority for the
 // duration of a block step: a SIMD holds two waves, and one that is computing
 // then goes ahead of one that is staging tiles or issuing its next loads,
 // whose latency the prefetch already covers (measured: 3-5% faster).
@@ -36,9 +39,11 @@
 //                         loads into swizzled unpadded rows (see its
 //                         specialization below); D = 64 stages them through
 //                         registers like the single kernel.
-// The forward is bound by K/V tile traffic from beyond L2 (each kept pair
-// reads a 32 KB tile pair); sharing tiles between the two blocks of a pair
-// removes the loads of their common blocks.
+// The one-block kernel is bound by K/V tile traffic from beyond L2 (each kept
+// pair reads a 32 KB tile pair); sharing tiles between the two blocks of a
+// pair removes the loads of their common blocks, after which the pair kernel
+// is bound by its block step (the softmax VALU work that does not co-issue
+// with MFMA) and by waits on union steps that only one block keeps.
 
 #include "common.h"
 #include "kernels.h"
@@ -97,6 +102,62 @@ __device__ __forceinline__ float pair_max(float x) {
     return __builtin_fmaxf(x, __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
 }
 
+// Online softmax of one block for query column c (keys split over this lane
+// and lane ^ 32), with the output rescaled only when some row's maximum grows
+// by more than 2^8 (probabilities then stay at most 2^8). The exponentials are
+// first taken against the running maximum: each is >= 0, so a lane sum of at
+// most 2^7 bounds all of its probabilities by 2^7, and a maximum that grew by
+// more than 2^8 would have given a probability near 2^8 or above (the margin
+// covers the rounding of the scaled logit and of exp2). Only when some lane's
+// sum exceeds 2^7 (or is not finite, as on a row's first block) is the block
+// maximum formed; if it grew by more than 2^8 the output is rescaled and the
+// exponentials are taken again. The running maximum, and so every result, is
+// the same as forming the block maximum first on every block.
+template <int D>
+__device__ __forceinline__ void softmax_lazy(RowState<D>& st, const f32x16_t (&s)[2], uint32_t (&pw)[2][8],
+                                             float& rs, float& ws, float scale_log2) {
+    constexpr int DT = RowState<D>::DT;
+    const uint32_t ones_bf16x2 = 0x3f803f80u;
+    auto exps = [&]() {
+        rs = 0.f;
+        ws = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // One rounding (fused), as the contracted form elsewhere.
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][2 * e], scale_log2, -st.m_run));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][2 * e + 1], scale_log2, -st.m_run));
+                rs += p0 + p1;
+                pw[kt][e] = pack_bf16x2(p0, p1);
+                ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[kt][e]),
+                                                     __builtin_bit_cast(bf16x2_t, ones_bf16x2), ws, false);
+            }
+    };
+    exps();
+    if (__builtin_amdgcn_ballot_w64(!(rs <= 128.0f))) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[1][r]);
+        mx = pair_max(mx) * scale_log2;
+        const bool grow = mx > st.m_run + kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? mx : st.m_run;
+            const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+            st.l_run *= alpha;
+            st.w_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st.oacc[t][r] *= alpha;
+            st.m_run = m_new;
+            exps();
+        }
+    }
+}
+
 // One kept key block: K tile at kbase (lane base for the S^T A operand), V
 // tile at vbase (lane base for the transposing V^T reads).
 // DEEP: read the K fragments further ahead of their products (all of tile 0,
@@ -149,41 +210,9 @@ __device__ __forceinline__ void block_step(RowState<D>& st, const char* kbase, c
         }
     }
 
-    // Online softmax for query column c (keys split over this lane and lane ^ 32).
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[1][r]);
-    mx = pair_max(mx) * scale_log2;
-    // Rescale only when some row's maximum grew by more than 2^8; otherwise
-    // keep the old reference (probabilities then stay below 2^8).
-    const bool grow = mx > st.m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx : st.m_run;
-        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
-        st.l_run *= alpha;
-        st.w_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st.oacc[t][r] *= alpha;
-        st.m_run = m_new;
-    }
-    float rs = 0.f, ws = 0.f;
+    float rs, ws;
     uint32_t pw[2][8];  // bf16 probabilities, B operands of the PV product
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(s[kt][2 * e] * scale_log2 - st.m_run);
-            const float p1 = __builtin_amdgcn_exp2f(s[kt][2 * e + 1] * scale_log2 - st.m_run);
-            rs += p0 + p1;
-            pw[kt][e] = pack_bf16x2(p0, p1);
-            ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[kt][e]),
-                                                 __builtin_bit_cast(bf16x2_t, ones_bf16x2), ws,
-                                                 false);
-        }
+    softmax_lazy(st, s, pw, rs, ws, scale_log2);
     st.l_run += rs;
     st.w_run += ws;
 
@@ -553,37 +582,9 @@ __device__ __forceinline__ void block_step_swz(RowState<128>& st, const char* kt
         }
         __builtin_amdgcn_sched_group_barrier(0x008, KK, 0);
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[1][r]);
-    mx = pair_max(mx) * scale_log2;
-    const bool grow = mx > st.m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx : st.m_run;
-        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
-        st.l_run *= alpha;
-        st.w_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st.oacc[t][r] *= alpha;
-        st.m_run = m_new;
-    }
-    float rs = 0.f, ws = 0.f;
+    float rs, ws;
     uint32_t pw[2][8];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(s[kt][2 * e] * scale_log2 - st.m_run);
-            const float p1 = __builtin_amdgcn_exp2f(s[kt][2 * e + 1] * scale_log2 - st.m_run);
-            rs += p0 + p1;
-            pw[kt][e] = pack_bf16x2(p0, p1);
-            ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[kt][e]),
-                                                 __builtin_bit_cast(bf16x2_t, ones_bf16x2), ws, false);
-        }
+    softmax_lazy(st, s, pw, rs, ws, scale_log2);
     st.l_run += rs;
     st.w_run += ws;
 #pragma unroll

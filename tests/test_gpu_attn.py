@@ -94,6 +94,34 @@ def test_fwd_random_masks(B, H, n, D, p, out_dtype):
     _fwd_check(q, k, v, _lists_from_mask(mask, B, H), mask, tag="random", out_dtype=out_dtype)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_running_maximum_growth(D):
+    """Key blocks scaled so that each row's maximum logit moves by different amounts from
+    block to block (about 4.3 log2 units per unit of scale step): steps where it grows by
+    more than 2^8 (the output is rescaled), steps where probabilities against the running
+    maximum exceed 2^7 without such growth (the block maximum is formed and no rescale
+    follows), and steps where it falls. Compared with the oracle, unpaired and paired, and
+    the two launches bitwise."""
+    nb = _nb()
+    n, H = 16, 2
+    S = 64 * n
+    scales = [0.5, 0.6, 1.5, 2.0, 4.5, 4.6, 5.8, 8.5, 8.0, 9.5, 3.0, 9.6, 11.0, 1.0, 12.5, 12.6]
+    g = torch.Generator().manual_seed(41 + D)
+    q = torch.randn((1, H, S, D), generator=g)
+    k = torch.randn((1, H, S, D), generator=g) * torch.tensor(scales).repeat_interleave(64).view(1, 1, S, 1)
+    v = torch.randn((1, H, S, D), generator=g)
+    q, k, v = (t.bfloat16() for t in (q, k, v))
+    mask = np.ones((H, n, n), dtype=np.uint8)
+    mask[1] = _random_mask(1, n, 5, 0.6)[0]
+    lists = _lists_from_mask(mask, 1, H)
+    o, lse = _fwd_check(q, k, v, lists, mask, tag=f"growing maxima D={D}", out_dtype=torch.float32)
+    o2, lse2 = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"],
+                                        out_dtype=torch.float32, frame_blocks=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
 def test_fwd_keep_all_equals_dense_and_custom_scale():
     q, k, v, _ = _rand(1, 2, 64 * 12, 128, seed=11, scale=2.0)
     mask = np.ones((2, 12, 12), dtype=np.uint8)

@@ -168,7 +168,6 @@ __device__ __forceinline__ void block_step(RowState<D>& st, const char* kbase, c
                                            float scale_log2) {
     using T = Tile<D>;
     constexpr int KK = RowState<D>::KK, DT = RowState<D>::DT;
-    const uint32_t ones_bf16x2 = 0x3f803f80u;
     __builtin_amdgcn_s_setprio(1);  // back to 0 at the end of the step
 
     // S^T (64 keys x 32 queries) as two 32 x 32 tiles.
@@ -556,7 +555,6 @@ __device__ __forceinline__ void block_step_swz(RowState<128>& st, const char* kt
                                                const uint32_t (&kl)[8], const uint32_t (&vl)[4],
                                                float scale_log2) {
     constexpr int KK = 8, DT = 4;
-    const uint32_t ones_bf16x2 = 0x3f803f80u;
     __builtin_amdgcn_s_setprio(1);
     // S^T: all of key tile 0's K fragments read first, then tile 1's reads
     // interleaved with tile 0's products (order pinned with scheduling groups).

@@ -150,12 +150,26 @@ def test_mask_map_in_head_chunks():
         res = _check_cdf_rows(p[h], dense[h].astype(bool), thr)
         print(f"[chunks] head {h}: kept {int(cnt[0, h].sum())}, CDF rule check {res}", flush=True)
         assert res["unexplained"] == 0, (h, res)
+    # The Top-k selector through the same chunks: keep j iff fewer than k entries of
+    # its row are strictly larger in the oracle's fp64 map.
+    topk = 300
+    outk = nb.nabla_build_topk_mask(qg, kg, topk, dense=True)
+    torch.cuda.synchronize()
+    densek = outk["dense_mask"].cpu().numpy().reshape(H, n, n).astype(bool)
+    for h in range(H):
+        asc = np.sort(p[h], axis=1)
+        above = np.stack([n - np.searchsorted(asc[i], p[h][i], side="right") for i in range(n)])
+        np.testing.assert_array_equal(above < topk, densek[h])
+    print(f"[chunks] top-{topk}: kept {int(densek.sum())}", flush=True)
     del p
     for h in range(H):
         one = nb.nabla_build_mask(qg[:, h:h + 1].contiguous(), kg[:, h:h + 1].contiguous(), thr)
+        onek = nb.nabla_build_topk_mask(qg[:, h:h + 1].contiguous(), kg[:, h:h + 1].contiguous(), topk)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(
             lists_to_mask(one["kv_count"].cpu().numpy(), one["kv_idx"].cpu().numpy())[0], dense[h])
+        np.testing.assert_array_equal(
+            lists_to_mask(onek["kv_count"].cpu().numpy(), onek["kv_idx"].cpu().numpy())[0].astype(bool), densek[h])
 
 
 def test_rows_beyond_the_maximum_are_rejected():

@@ -769,11 +769,12 @@ def main() -> int:
             "algorithmic_flop_per_launch": step_flops,
             "note": "forward call = pair-count kernel + per-head longest-first ordering kernel + the "
                     "attention kernel, events bracket all three; peak assumes 2.4 GHz while the GPU "
-                    "runs at ~1.9 GHz under this load (counters: MFMA busy ~42% of SIMD cycles); the "
-                    "kernel is limited by its per-block step (~130 non-transcendental softmax VALU "
-                    "instructions per step that do not co-issue with MFMA) and by waits on union "
-                    "steps only one block of a pair keeps, not by LDS (~21% busy) or by its traffic "
-                    "beyond L2 (see traffic; ~5.5 TB/s, below the ~7 TB/s the one-block kernel sustains)",
+                    "runs at ~1.8-1.9 GHz under this load (counters: MFMA busy ~49% of SIMD cycles, "
+                    "1/16 of it the MFMA weight sums); the kernel is limited by its per-block step "
+                    "(~85 non-transcendental softmax VALU instructions per step that co-issue with "
+                    "MFMA only in part) and by waits on union steps only one block of a pair keeps, "
+                    "not by LDS (~21% busy) or by its traffic beyond L2 (see traffic; ~5.5 TB/s, "
+                    "below the ~7 TB/s the one-block kernel sustains)",
         },
         "cpu_baseline": None,
         "context": {

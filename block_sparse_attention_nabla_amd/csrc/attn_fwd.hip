@@ -20,7 +20,10 @@
 // row maximum grows by more than 2^8; the block maximum is formed only when
 // the exponentials taken against the running maximum could have reached that
 // (softmax_lazy), which leaves every result unchanged and keeps the max
-// reduction out of most steps. A wave raises its issue priority for the
+// reduction out of most steps. The output is divided by the sum of the bf16
+// weights that entered the PV product (LSE uses the fp32 sum); that sum comes
+// from four small MFMAs per block on the PV product's own B operands
+// (weight_sum_operand). A wave raises its issue priority for the
 // duration of a block step: a SIMD holds two waves, and one that is computing
 // then goes ahead of one that is staging tiles or issuing its next loads,
 // whose latency the prefetch already covers (measured: 3-5% faster).
@@ -73,11 +76,14 @@ struct RowState {
     bf16x8_t qf[KK];                   // Q^T as the B operand
     f32x16_t oacc[DT];                 // O^T accumulators
     // m_run: running maximum (log2 units), equal in both lanes of a query
-    // column; l_run: sum of fp32 probabilities (for LSE); w_run: sum of the
-    // bf16-rounded probabilities that feed the PV product (the output's
-    // normaliser). l_run and w_run are this lane's share of the column's keys;
-    // the epilogue adds the two lanes' shares.
-    float m_run, l_run, w_run;
+    // column; l_run: sum of fp32 probabilities (for LSE), this lane's share of
+    // the column's keys (the epilogue adds the two lanes' shares); w_run: sum
+    // of the bf16-rounded probabilities that feed the PV product (the
+    // output's normaliser) over all of the column's keys, in both lanes, up to
+    // the previous block; w_pend: the last block's weight sum, added at the
+    // start of the next block (its MFMA has finished by then; read at the end
+    // of its own block it would stall the wave until the PV products drain).
+    float m_run, l_run, w_run, w_pend;
 };
 
 // Lane l of a wave: query column c = l % 32, half h = l / 32.
@@ -91,6 +97,7 @@ __device__ __forceinline__ void load_rows(RowState<D>& st, const uint16_t* qrow_
     st.m_run = -INFINITY;
     st.l_run = 0.f;
     st.w_run = 0.f;
+    st.w_pend = 0.f;
 }
 
 // Maximum over the lane pair (l, l ^ 32) that holds one query column: the
@@ -115,12 +122,10 @@ __device__ __forceinline__ float pair_max(float x) {
 // the same as forming the block maximum first on every block.
 template <int D>
 __device__ __forceinline__ void softmax_lazy(RowState<D>& st, const f32x16_t (&s)[2], uint32_t (&pw)[2][8],
-                                             float& rs, float& ws, float scale_log2) {
+                                             float& rs, float scale_log2) {
     constexpr int DT = RowState<D>::DT;
-    const uint32_t ones_bf16x2 = 0x3f803f80u;
     auto exps = [&]() {
         rs = 0.f;
-        ws = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -130,8 +135,6 @@ __device__ __forceinline__ void softmax_lazy(RowState<D>& st, const f32x16_t (&s
                 const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][2 * e + 1], scale_log2, -st.m_run));
                 rs += p0 + p1;
                 pw[kt][e] = pack_bf16x2(p0, p1);
-                ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[kt][e]),
-                                                     __builtin_bit_cast(bf16x2_t, ones_bf16x2), ws, false);
             }
     };
     exps();
@@ -158,6 +161,30 @@ __device__ __forceinline__ void softmax_lazy(RowState<D>& st, const f32x16_t (&s
     }
 }
 
+// Sum of the bf16 weights by MFMA. v_mfma_f32_16x16x32_bf16 reads B (32 x 16)
+// as lane l = 16 g + n supplying column n, k-slots 8 g .. 8 g + 7, and A
+// (16 x 32) as lane l supplying row l % 16 at the same k-slots; lane l gets
+// C[4 g + i][n], i = 0..3. Fed with the PV product's B operand of one 16-key
+// slice, whose lane l holds 8 weights of query column l % 32 (half l / 32 of
+// the slice's keys), the slots of group g belong to query n + 16 (g % 2). An
+// A operand of ones at slot groups g with g % 2 == (row / 4) % 2 and zeros
+// elsewhere -- in lane l, ones iff bit 4 of l equals bit 2 -- makes every
+// C[4 g + i][n] the slice's full weight sum of query n + 16 (g % 2), which is
+// lane l's own column l % 32. Four such products per block replace 16
+// v_dot2c_f32_bf16, which do not co-execute with MFMA. Both helpers give the
+// same operand: the second reads the lane id through an opaque instruction, so
+// a kernel without registers to spare rebuilds it at each use instead of
+// holding four registers across its loop.
+__device__ __forceinline__ bf16x8_t weight_sum_operand(uint32_t l) {
+    const uint32_t w = ((l >> 4) & 1) == ((l >> 2) & 1) ? 0x3f803f80u : 0u;
+    return as_bf16x8(make_uint4(w, w, w, w));
+}
+__device__ __forceinline__ bf16x8_t weight_sum_operand_here() {
+    uint32_t l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return weight_sum_operand(l);
+}
+
 // One kept key block: K tile at kbase (lane base for the S^T A operand), V
 // tile at vbase (lane base for the transposing V^T reads).
 // DEEP: read the K fragments further ahead of their products (all of tile 0,
@@ -165,10 +192,11 @@ __device__ __forceinline__ void softmax_lazy(RowState<D>& st, const f32x16_t (&s
 // scheduling groups) -- 15 more registers; used where they fit 2 waves/SIMD.
 template <int D, bool DEEP>
 __device__ __forceinline__ void block_step(RowState<D>& st, const char* kbase, const char* vbase,
-                                           float scale_log2) {
+                                           float scale_log2, bf16x8_t wsel) {
     using T = Tile<D>;
     constexpr int KK = RowState<D>::KK, DT = RowState<D>::DT;
     __builtin_amdgcn_s_setprio(1);  // back to 0 at the end of the step
+    st.w_run += st.w_pend;
 
     // S^T (64 keys x 32 queries) as two 32 x 32 tiles.
     f32x16_t s[2];
@@ -209,11 +237,11 @@ __device__ __forceinline__ void block_step(RowState<D>& st, const char* kbase, c
         }
     }
 
-    float rs, ws;
+    float rs;
     uint32_t pw[2][8];  // bf16 probabilities, B operands of the PV product
-    softmax_lazy(st, s, pw, rs, ws, scale_log2);
+    softmax_lazy(st, s, pw, rs, scale_log2);
     st.l_run += rs;
-    st.w_run += ws;
+    f32x4_t wsum = {0.f, 0.f, 0.f, 0.f};
 
     // O^T += V^T P^T. For key tile kt and half u, B = S^T registers 8u..8u+7:
     // slot s is key 32kt + 16u + 8*(s/4) + 4h + s%4; the transposing reads
@@ -224,6 +252,7 @@ __device__ __forceinline__ void block_step(RowState<D>& st, const char* kbase, c
         for (int u = 0; u < 2; ++u) {
             const bf16x8_t b = as_bf16x8(make_uint4(pw[kt][4 * u], pw[kt][4 * u + 1],
                                                     pw[kt][4 * u + 2], pw[kt][4 * u + 3]));
+            wsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wsel, b, wsum, 0, 0, 0);
             const char* vrow = vbase + (32 * kt + 16 * u) * T::VSTB;
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
@@ -237,6 +266,7 @@ __device__ __forceinline__ void block_step(RowState<D>& st, const char* kbase, c
                                            st.oacc[t]);
             }
         }
+    st.w_pend = wsum[0];
     __builtin_amdgcn_s_setprio(0);
 }
 
@@ -247,7 +277,7 @@ __device__ __forceinline__ void store_rows(const RowState<D>& st, int64_t head, 
                                            void* __restrict__ o, int o_fp32, float* __restrict__ lse,
                                            int64_t lse_index) {
     constexpr int DT = RowState<D>::DT;
-    const float w_sum = st.w_run + __shfl_xor(st.w_run, 32);
+    const float w_sum = st.w_run + st.w_pend;
     const float l_sum = st.l_run + __shfl_xor(st.l_run, 32);
     const float inv_l = w_sum > 0.f ? 1.0f / w_sum : 0.f;
     if (o_fp32) {
@@ -355,7 +385,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_kernel(
         __syncthreads();
     }
     for (int it = 0; it < cnt; ++it) {
-        block_step<D, false>(st, kbase, vbase, scale_log2);
+        block_step<D, false>(st, kbase, vbase, scale_log2, weight_sum_operand_here());
         if (it + 1 < cnt) {
             __syncthreads();  // every wave has read K_j and V_j
             NABLA_STAGE();  // block it+1, fetched one iteration ago
@@ -421,6 +451,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
     const int64_t qrow = (int64_t)(active ? my_qb : qa) * kBlockN + (wave & 1) * 32 + c;
     RowState<D> st;
     load_rows<D>(st, q + head + qrow * D, h);
+    const bf16x8_t wsel = weight_sum_operand(lane);
 
     // Union cursor: positions in both lists; the next element of each (n = end).
     struct Cursor {
@@ -482,7 +513,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel(
         __syncthreads();
         for (;;) {
             const int mine = grp ? (f_cur & 2) : (f_cur & 1);
-            if (mine && active) block_step<D, true>(st, kbase + buf * KB, vbase + buf * VB, scale_log2);
+            if (mine && active)
+                block_step<D, true>(st, kbase + buf * KB, vbase + buf * VB, scale_log2, wsel);
             if (f_next == 0) break;  // the computed step was the last one
             // The other buffer's readers finished before the last barrier.
             NABLA_PSTAGE(buf ^ 1);  // the step fetched one iteration ago
@@ -553,9 +585,10 @@ __device__ __forceinline__ void settle_v(T_& x) { asm volatile("" : "+v"(x)); }
 // second 32-key tile), V transposing reads at vl[t] (+ row offsets).
 __device__ __forceinline__ void block_step_swz(RowState<128>& st, const char* kt0, const char* vt0,
                                                const uint32_t (&kl)[8], const uint32_t (&vl)[4],
-                                               float scale_log2) {
+                                               float scale_log2, bf16x8_t wsel) {
     constexpr int KK = 8, DT = 4;
     __builtin_amdgcn_s_setprio(1);
+    st.w_run += st.w_pend;
     // S^T: all of key tile 0's K fragments read first, then tile 1's reads
     // interleaved with tile 0's products (order pinned with scheduling groups).
     f32x16_t s[2];
@@ -580,17 +613,18 @@ __device__ __forceinline__ void block_step_swz(RowState<128>& st, const char* kt
         }
         __builtin_amdgcn_sched_group_barrier(0x008, KK, 0);
     }
-    float rs, ws;
+    float rs;
     uint32_t pw[2][8];
-    softmax_lazy(st, s, pw, rs, ws, scale_log2);
+    softmax_lazy(st, s, pw, rs, scale_log2);
     st.l_run += rs;
-    st.w_run += ws;
+    f32x4_t wsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const bf16x8_t b = as_bf16x8(make_uint4(pw[kt][4 * u], pw[kt][4 * u + 1],
                                                     pw[kt][4 * u + 2], pw[kt][4 * u + 3]));
+            wsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wsel, b, wsum, 0, 0, 0);
             const char* vrow = vt0 + (32 * kt + 16 * u) * 256;
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
@@ -601,6 +635,7 @@ __device__ __forceinline__ void block_step_swz(RowState<128>& st, const char* kt
                 st.oacc[t] = mfma_32x32x16(as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y)), b, st.oacc[t]);
             }
         }
+    st.w_pend = wsum[0];
     __builtin_amdgcn_s_setprio(0);
 }
 }  // namespace
@@ -648,6 +683,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel<128>(
     const int64_t qrow = (int64_t)(active ? my_qb : qa) * kBlockN + (wave & 1) * 32 + c;
     RowState<D> st;
     load_rows<D>(st, q + head + qrow * D, h);
+    const bf16x8_t wsel = weight_sum_operand(lane);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) settle_v(st.qf[kk]);
 
@@ -709,7 +745,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_pair_kernel<128>(
             // Next step's tiles; with no next step, any valid block (never read).
             dma(f_nxt ? j_nxt : (f_cur ? j_cur : 0), nk, nv);
             const int mine = grp ? (f_cur & 2) : (f_cur & 1);
-            if (mine && active) block_step_swz(st, ck, cv, kl, vl, scale_log2);
+            if (mine && active) block_step_swz(st, ck, cv, kl, vl, scale_log2, wsel);
             j_cur = j_nxt;
             f_cur = f_nxt;
             if (f_cur) adv(j_nxt, f_nxt);

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     __shared__ __attribute__((aligned(16))) char sQ[kBlockN * T::RSTB];
     __shared__ __attribute__((aligned(16))) char sO[kBlockN * T::RSTB];
     __shared__ __attribute__((aligned(16))) float sL[kBlockN];
-    __shared__ __attribute__((aligned(16))) float sDel[kBlockN];
+    __shared__ __attribute__((aligned(16))) float sDel[kBlockN];  // -Delta of the staged rows
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, c = lane & 31;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
         NABLA_BWD_STAGE(sQ, sO);
         if (tid < kBlockN) {
             sL[tid] = rl * kLog2e;
-            sDel[tid] = rd;
+            sDel[tid] = -rd;
         }
         if (cnt > 1) {
             int i1 = list[1];
@@ -248,7 +248,16 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             // S and dP tiles: rows = queries 32 qt + c_row(r, h), column = key c of this wave.
-            f32x16_t sc = zero16(), dp = zero16();
+            f32x16_t sc = zero16(), dp;
+            // dP starts from -Delta of its rows, so the products yield dP - Delta.
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 d4 = *reinterpret_cast<const float4*>(sDel + 32 * qt + 8 * g + 4 * h);
+                dp[4 * g + 0] = d4.x;
+                dp[4 * g + 1] = d4.y;
+                dp[4 * g + 2] = d4.z;
+                dp[4 * g + 3] = d4.w;
+            }
             {
                 bf16x8_t a[KK];
 #pragma unroll
@@ -269,15 +278,13 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float4 l4 = *reinterpret_cast<const float4*>(sL + 32 * qt + 8 * g + 4 * h);
-                const float4 d4 = *reinterpret_cast<const float4*>(sDel + 32 * qt + 8 * g + 4 * h);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
                     const float p = __builtin_amdgcn_exp2f(sc[r] * scale_log2 - lv[e]);
                     sc[r] = p;
-                    dp[r] = p * (dp[r] - dv4[e]);
+                    dp[r] = p * dp[r];
                 }
             }
 #pragma unroll
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
             NABLA_BWD_STAGE(sQ, sO);
             if (tid < kBlockN) {
                 sL[tid] = rl * kLog2e;
-                sDel[tid] = rd;
+                sDel[tid] = -rd;
             }
             if (it + 2 < cnt) {
                 int i2 = list[it + 2];

@@ -420,7 +420,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
         uint32_t dsw[8];
         {
             // S^T and dP^T quadrant: rows = keys 32 kh + c_row(r, h), column = query c.
-            f32x16_t sc = zero16(), dp = zero16();
+            // dP^T starts from -Delta (a loop invariant: the compiler keeps it in
+            // registers), so the products yield dP - Delta.
+            f32x16_t sc = zero16(), dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[r] = -del;
             {
                 bf16x8_t a[KK];
 #pragma unroll
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = __builtin_amdgcn_exp2f(sc[r] * scale_log2 - l2);
-                dp[r] = p * (dp[r] - del);
+                dp[r] = p * dp[r];
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) dsw[e] = pack_bf16x2(dp[2 * e], dp[2 * e + 1]);
@@ -624,7 +628,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel<128>(
     auto compute = [&](const char* sK, const char* sV) {
         uint32_t dsw[8];
         {
-            f32x16_t sc = zero16(), dp = zero16();
+            // dP^T starts from -Delta (a loop invariant: the compiler keeps it in
+            // registers), so the products yield dP - Delta.
+            f32x16_t sc = zero16(), dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[r] = -del;
             {
                 bf16x8_t a[KK];
 #pragma unroll
@@ -642,7 +650,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel<128>(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = __builtin_amdgcn_exp2f(sc[r] * scale_log2 - l2);
-                dp[r] = p * (dp[r] - del);
+                dp[r] = p * dp[r];
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) dsw[e] = pack_bf16x2(dp[2 * e], dp[2 * e + 1]);

@@ -122,6 +122,38 @@ def test_fwd_running_maximum_growth(D):
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_constant_values_are_reproduced(D):
+    """The weights of each softmax row of eq. (4) (section 2.2) sum to one, so values that
+    are the same for every token come out unchanged: O[s, d] = c[d] for every row with a
+    kept block. The kernel divides by the sum of the bf16 weights that actually entered the
+    PV product, so only fp32 accumulation rounding remains (a division by the fp32 sum of
+    the unrounded weights would leave the bf16 rounding of the weights, up to 2^-8 of c).
+    Keys scaled as in the running-maximum test, so rescales of the output and the lazy
+    block maximum are exercised; unpaired and paired launches."""
+    nb = _nb()
+    n, H = 16, 2
+    S = 64 * n
+    scales = [0.5, 0.6, 1.5, 2.0, 4.5, 4.6, 5.8, 8.5, 8.0, 9.5, 3.0, 9.6, 11.0, 1.0, 12.5, 12.6]
+    g = torch.Generator().manual_seed(77 + D)
+    q = torch.randn((1, H, S, D), generator=g).bfloat16()
+    k = (torch.randn((1, H, S, D), generator=g)
+         * torch.tensor(scales).repeat_interleave(64).view(1, 1, S, 1)).bfloat16()
+    c = (torch.randn((1, H, 1, D), generator=g) * 3.0).bfloat16()
+    v = c.expand(1, H, S, D).contiguous()
+    mask = np.ones((H, n, n), dtype=np.uint8)
+    mask[1] = _random_mask(1, n, 9, 0.5)[0]
+    lists = _lists_from_mask(mask, 1, H)
+    want = c.float().expand(1, H, S, D)
+    for F in (0, 4):
+        o, _ = nb.nabla_sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), lists["kv_count"], lists["kv_idx"],
+                                        out_dtype=torch.float32, frame_blocks=F)
+        torch.cuda.synchronize()
+        rel = ((o.cpu() - want).abs() / want.abs().clamp_min(1e-30)).max().item()
+        print(f"[fwd] constant values D={D} F={F}: max relative deviation {rel:.2e}", flush=True)
+        assert rel <= 3e-5, rel
+
+
 def test_fwd_keep_all_equals_dense_and_custom_scale():
     q, k, v, _ = _rand(1, 2, 64 * 12, 128, seed=11, scale=2.0)
     mask = np.ones((2, 12, 12), dtype=np.uint8)

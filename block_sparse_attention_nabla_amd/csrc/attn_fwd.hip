@@ -125,7 +125,7 @@ __device__ __forceinline__ void softmax_lazy(RowState<D>& st, const f32x16_t (&s
                                              float& rs, float scale_log2) {
     constexpr int DT = RowState<D>::DT;
     auto exps = [&]() {
-        rs = 0.f;
+        rs = -0.f;  // x + (-0) == x for every x, so the first add folds away
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll

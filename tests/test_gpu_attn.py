@@ -304,6 +304,40 @@ def _bwd_check(q, k, v, do, lists, mask, tag="", q_blocks=None, kv_blocks=None,
     return dq, dk, dv
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_constant_values_give_zero_dq_dk(D):
+    """Gradients of eq. (4) (section 2.2) when the values are the same for every token: the
+    output does not depend on the attention weights, so dQ = dK = 0 exactly, while
+    dV_j = sum_i P_ij dO_i. Here dP_ij = dO_i . c is the same for every key and equals
+    Delta_i = dO_i . O_i, so the kernels' dP - Delta (the dP products accumulated from
+    -Delta) must cancel to fp32 rounding. dQ and dK are checked against a bound far below
+    their size with non-constant values; dV against the oracle."""
+    nb = _nb()
+    n, H = 12, 2
+    S = 64 * n
+    g = torch.Generator().manual_seed(91 + D)
+    q = (torch.randn((1, H, S, D), generator=g) * 1.5).bfloat16()
+    k = (torch.randn((1, H, S, D), generator=g) * 1.5).bfloat16()
+    c = (torch.randn((1, H, 1, D), generator=g) * 2.0).bfloat16()
+    v = c.expand(1, H, S, D).contiguous()
+    do = torch.randn((1, H, S, D), generator=g).bfloat16()
+    mask = np.ones((H, n, n), dtype=np.uint8)
+    mask[1] = _random_mask(1, n, 13, 0.5)[0]
+    lists = _lists_from_mask(mask, 1, H)
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = nb.nabla_sparse_attn_fwd(qg, kg, vg, lists["kv_count"], lists["kv_idx"], out_dtype=torch.float32)
+    dq, dk, dv = nb.nabla_sparse_attn_bwd(qg, kg, vg, o, dog, lse, lists["kv_count"], lists["kv_idx"],
+                                          lists["q_count"], lists["q_idx"])
+    torch.cuda.synchronize()
+    mdq, mdk = dq.float().abs().max().item(), dk.float().abs().max().item()
+    rdq, rdk, rdv = oracle.attn_bwd(q.float(), k.float(), v.float(), do.float(), mask, 64)
+    e = grad_errors(dv.float().cpu().numpy().reshape(H, S, D), rdv)
+    print(f"[bwd] constant values D={D}: max|dQ| {mdq:.2e} max|dK| {mdk:.2e} "
+          f"(oracle {np.abs(rdq).max():.1e}, {np.abs(rdk).max():.1e}); dV {e}", flush=True)
+    assert mdq <= 2e-3 and mdk <= 2e-3, (mdq, mdk)
+    assert grad_ok(e), e
+
+
 @pytest.mark.parametrize("thr", [0.5, 1.0])
 def test_bwd_tiny_with_gpu_mask(thr):
     nb = _nb()

@@ -155,14 +155,26 @@ __global__ __launch_bounds__(256) void delta_kernel(const void* __restrict__ o,
     } while (0)
 
 // ---------------------------------------------------------------------------
-// dK, dV for one 64-key block; wave w owns keys 32w .. 32w+31.
-// Per query block i: S = Q_i K^T and dP = dO_i V^T (A = Q_i / dO_i rows from
-// LDS, B = K^T / V^T in registers; accumulator rows = queries), then
-// dV^T += dO_i^T P and dK^T += Q_i^T dS (A = transposed reads of the dO_i / Q_i
-// tiles, B = P / dS from the accumulators).
+// dK, dV for one 64-key block on four waves. Wave w takes key half
+// kh = w % 2 (keys 32 kh .. +31) and query half qh = w / 2. Per query block i
+// of the key block's list:
+//   1. S = Q_i K^T and dP = dO_i V^T for the quadrant (queries 32 qh .. +31) x
+//      (its keys): A = Q_i / dO_i rows from LDS, B = K^T / V^T in registers,
+//      accumulator rows = queries; P and dS = P * (dP - Delta) packed to bf16.
+//   2. The packed quadrant goes to LDS; the wave with the same keys and the
+//      other query half reads it back in the same lane layout (its lanes hold
+//      the same key columns), so both then hold P and dS for all 64 queries.
+//   3. dV^T += dO_i^T P and dK^T += Q_i^T dS for half of the head dimension,
+//      d in [D/2 qh, D/2 (qh + 1)) (A = transposed reads of the dO_i / Q_i
+//      tiles, B = P / dS).
+// A wave thus holds half of the dK/dV accumulators of its keys (about 250
+// registers), so two workgroups -- two waves per SIMD -- share a CU and one
+// wave's products overlap the other's softmax. Every output element gets the
+// same products in the same order as in a wave owning all of D: the split
+// changes no result.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(128) void dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta, int S, int n,
@@ -170,15 +182,19 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     const int32_t* __restrict__ order, XcdSchedule sched, float scale, float scale_log2,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     using T = BTile<D>;
-    constexpr int NT = 128;
-    constexpr int KK = D / 16, DT = D / 32, L = T::template loads<NT>();
+    constexpr int NT = 256;
+    constexpr int KK = D / 16, DT = D / 32, DH = DT / 2, L = T::template loads<NT>();
     __shared__ __attribute__((aligned(16))) char sQ[kBlockN * T::RSTB];
     __shared__ __attribute__((aligned(16))) char sO[kBlockN * T::RSTB];
     __shared__ __attribute__((aligned(16))) float sL[kBlockN];
     __shared__ __attribute__((aligned(16))) float sDel[kBlockN];  // -Delta of the staged rows
+    // Packed P (groups 0, 1) and dS (groups 2, 3) of each wave's quadrant,
+    // [wave][group][lane]: lane-contiguous 16-byte words.
+    __shared__ __attribute__((aligned(16))) u32x4_t sX[4][4][kWave];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, c = lane & 31;
+    const int kh = wave & 1, qh = wave >> 1;
     const int64_t item = scheduled_item(sched, order, blockIdx.x);
     if (item < 0) return;  // padding slot (whole workgroup)
     const int64_t bh = item / n;
@@ -187,13 +203,13 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     cnt = cnt < 0 ? 0 : (cnt > n ? n : cnt);
     const int32_t* list = q_idx + item * (int64_t)n;
     const int64_t head = bh * (int64_t)S * D;
-    const uint16_t* qh = q + head;
-    const uint16_t* oh = d_o + head;
+    const uint16_t* qh_ptr = q + head;
+    const uint16_t* oh_ptr = d_o + head;
     const float* lh = lse + bh * (int64_t)S;
     const float* dh = delta + bh * (int64_t)S;
 
     // K^T and V^T as B operands: lane holds key krow, d = 16 kk + 8 h + 0..7.
-    const int krow = kb * kBlockN + wave * 32 + c;
+    const int krow = kb * kBlockN + kh * 32 + c;
     bf16x8_t kf[KK], vf[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -205,24 +221,28 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
         settle(kf[kk]);
         settle(vf[kk]);
     }
-    f32x16_t dVt[DT], dKt[DT];
+    f32x16_t dVt[DH], dKt[DH];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
+    for (int t = 0; t < DH; ++t) {
         dVt[t] = zero16();
         dKt[t] = zero16();
     }
 
-    const char* qrow_base = sQ + c * T::RSTB + 16 * h;  // row 32 qt + c, bytes 32 kk + 16 h
-    const char* orow_base = sO + c * T::RSTB + 16 * h;
-    const char* qtr = tr_lane_base(sQ, lane, T::RSTB);
-    const char* otr = tr_lane_base(sO, lane, T::RSTB);
+    // Rows 32 qh + c of the Q / dO tiles, bytes 32 kk + 16 h.
+    const char* qrow_base = sQ + (32 * qh + c) * T::RSTB + 16 * h;
+    const char* orow_base = sO + (32 * qh + c) * T::RSTB + 16 * h;
+    // Transposed reads of this wave's half of the head dimension.
+    const char* qtr = tr_lane_base(sQ, lane, T::RSTB) + 64 * DH * qh;
+    const char* otr = tr_lane_base(sO, lane, T::RSTB) + 64 * DH * qh;
+    const float* lrow = sL + 32 * qh + 4 * h;
+    const float* drow = sDel + 32 * qh + 4 * h;
 
     u32x4_t ra[L], rb[L];
     float rl = 0.f, rd = 0.f;  // LSE / Delta of one query row (threads < 64)
     if (cnt > 0) {
         int i0 = list[0];
         i0 = (unsigned)i0 < (unsigned)n ? i0 : 0;
-        NABLA_BWD_FETCH(qh, oh, i0);
+        NABLA_BWD_FETCH(qh_ptr, oh_ptr, i0);
         if (tid < kBlockN) {
             rl = lh[(int64_t)i0 * kBlockN + tid];
             rd = dh[(int64_t)i0 * kBlockN + tid];
@@ -235,7 +255,7 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
         if (cnt > 1) {
             int i1 = list[1];
             i1 = (unsigned)i1 < (unsigned)n ? i1 : 0;
-            NABLA_BWD_FETCH(qh, oh, i1);
+            NABLA_BWD_FETCH(qh_ptr, oh_ptr, i1);
             if (tid < kBlockN) {
                 rl = lh[(int64_t)i1 * kBlockN + tid];
                 rd = dh[(int64_t)i1 * kBlockN + tid];
@@ -243,16 +263,35 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
         }
         __syncthreads();
     }
-    for (int it = 0; it < cnt; ++it) {
-        uint32_t pw[2][8], dsw[2][8];
+    // dV^T += dO^T P, dK^T += Q^T dS over the query halves in order (p0/s0:
+    // queries 0..31, p1/s1: 32..63); slot s of B is query
+    // 32 qt + 16 u + 8 (s/4) + 4 h + s%4, matched by the transposed reads.
+    auto accumulate = [&](const uint32_t (&p0)[8], const uint32_t (&s0)[8], const uint32_t (&p1)[8],
+                          const uint32_t (&s1)[8]) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            // S and dP tiles: rows = queries 32 qt + c_row(r, h), column = key c of this wave.
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t* pp = qt == 0 ? p0 : p1;
+                const uint32_t* ss = qt == 0 ? s0 : s1;
+                const bf16x8_t bp = as_bf16x8(make_uint4(pp[4 * u], pp[4 * u + 1], pp[4 * u + 2], pp[4 * u + 3]));
+                const bf16x8_t bs = as_bf16x8(make_uint4(ss[4 * u], ss[4 * u + 1], ss[4 * u + 2], ss[4 * u + 3]));
+#pragma unroll
+                for (int t = 0; t < DH; ++t) {
+                    dVt[t] = mfma_32x32x16(tr_operand<T::RSTB>(otr, 32 * qt + 16 * u, t), bp, dVt[t]);
+                    dKt[t] = mfma_32x32x16(tr_operand<T::RSTB>(qtr, 32 * qt + 16 * u, t), bs, dKt[t]);
+                }
+            }
+    };
+    for (int it = 0; it < cnt; ++it) {
+        uint32_t pw[8], dsw[8];
+        {
+            // S and dP quadrant: rows = queries 32 qh + c_row(r, h), column = key c.
             f32x16_t sc = zero16(), dp;
             // dP starts from -Delta of its rows, so the products yield dP - Delta.
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 d4 = *reinterpret_cast<const float4*>(sDel + 32 * qt + 8 * g + 4 * h);
+                const float4 d4 = *reinterpret_cast<const float4*>(drow + 8 * g);
                 dp[4 * g + 0] = d4.x;
                 dp[4 * g + 1] = d4.y;
                 dp[4 * g + 2] = d4.z;
@@ -262,7 +301,7 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
                 bf16x8_t a[KK];
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow_base + 32 * qt * T::RSTB + 32 * kk));
+                    a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow_base + 32 * kk));
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) sc = mfma_32x32x16(a[kk], kf[kk], sc);
             }
@@ -270,14 +309,14 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
                 bf16x8_t a[KK];
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(orow_base + 32 * qt * T::RSTB + 32 * kk));
+                    a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(orow_base + 32 * kk));
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) dp = mfma_32x32x16(a[kk], vf[kk], dp);
             }
-            // Rows c_row(4g + e, h) = 32 qt + 8 g + 4 h + e: four consecutive rows per g.
+            // Rows c_row(4g + e, h) = 32 qh + 8 g + 4 h + e: four consecutive rows per g.
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *reinterpret_cast<const float4*>(sL + 32 * qt + 8 * g + 4 * h);
+                const float4 l4 = *reinterpret_cast<const float4*>(lrow + 8 * g);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -289,26 +328,30 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pw[qt][e] = pack_bf16x2(sc[2 * e], sc[2 * e + 1]);
-                dsw[qt][e] = pack_bf16x2(dp[2 * e], dp[2 * e + 1]);
+                pw[e] = pack_bf16x2(sc[2 * e], sc[2 * e + 1]);
+                dsw[e] = pack_bf16x2(dp[2 * e], dp[2 * e + 1]);
             }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS: slot s of B is query
-        // 32 qt + 16 u + 8 (s/4) + 4 h + s%4, matched by the transposed reads.
+        // Hand the quadrant to the wave with the same keys and the other query half.
+        sX[wave][0][lane] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+        sX[wave][1][lane] = u32x4_t{pw[4], pw[5], pw[6], pw[7]};
+        sX[wave][2][lane] = u32x4_t{dsw[0], dsw[1], dsw[2], dsw[3]};
+        sX[wave][3][lane] = u32x4_t{dsw[4], dsw[5], dsw[6], dsw[7]};
+        __syncthreads();
+        uint32_t po[8], so[8];
+        {
+            const u32x4_t x0 = sX[wave ^ 2][0][lane], x1 = sX[wave ^ 2][1][lane];
+            const u32x4_t x2 = sX[wave ^ 2][2][lane], x3 = sX[wave ^ 2][3][lane];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8_t bp = as_bf16x8(make_uint4(pw[qt][4 * u], pw[qt][4 * u + 1],
-                                                         pw[qt][4 * u + 2], pw[qt][4 * u + 3]));
-                const bf16x8_t bs = as_bf16x8(make_uint4(dsw[qt][4 * u], dsw[qt][4 * u + 1],
-                                                         dsw[qt][4 * u + 2], dsw[qt][4 * u + 3]));
-#pragma unroll
-                for (int t = 0; t < DT; ++t) {
-                    dVt[t] = mfma_32x32x16(tr_operand<T::RSTB>(otr, 32 * qt + 16 * u, t), bp, dVt[t]);
-                    dKt[t] = mfma_32x32x16(tr_operand<T::RSTB>(qtr, 32 * qt + 16 * u, t), bs, dKt[t]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                po[e] = x0[e];
+                po[4 + e] = x1[e];
+                so[e] = x2[e];
+                so[4 + e] = x3[e];
             }
+        }
+        if (qh == 0) accumulate(pw, dsw, po, so);
+        else accumulate(po, so, pw, dsw);
         if (it + 1 < cnt) {
             __syncthreads();  // every wave is done with this query block's tiles
             NABLA_BWD_STAGE(sQ, sO);
@@ -319,7 +362,7 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
             if (it + 2 < cnt) {
                 int i2 = list[it + 2];
                 i2 = (unsigned)i2 < (unsigned)n ? i2 : 0;
-                NABLA_BWD_FETCH(qh, oh, i2);
+                NABLA_BWD_FETCH(qh_ptr, oh_ptr, i2);
                 if (tid < kBlockN) {
                     rl = lh[(int64_t)i2 * kBlockN + tid];
                     rd = dh[(int64_t)i2 * kBlockN + tid];
@@ -328,8 +371,8 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
             __syncthreads();
         }
     }
-    store_t_acc<DT>(dk + head + (int64_t)krow * D, dKt, scale, h);
-    store_t_acc<DT>(dv + head + (int64_t)krow * D, dVt, 1.0f, h);
+    store_t_acc<DH>(dk + head + (int64_t)krow * D + 32 * DH * qh, dKt, scale, h);
+    store_t_acc<DH>(dv + head + (int64_t)krow * D + 32 * DH * qh, dVt, 1.0f, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -705,6 +748,238 @@ __global__ __launch_bounds__(256, 2) void dq_kernel<128>(
     }
 }
 
+// ---------------------------------------------------------------------------
+// dkdv_kernel for D = 128: the same quadrants and products in the same order
+// (bitwise equal results), with the Q/dO tiles moved by direct-to-LDS loads
+// into two buffers as in dq_kernel<128> (both tiles are read row-wise and
+// transposed, so both use the K swizzle), and the second product split by
+// output instead of by head dimension: the query-half-0 wave of a key half
+// accumulates dV over all of D and the query-half-1 wave dK. Each wave then
+// needs the other wave's half of only one of P and dS (the dV wave receives
+// P, the dK wave dS), which halves the exchange and lets two workgroups fit
+// the LDS. LSE and -Delta of the staged rows are double-buffered with the
+// tiles (written by wave 0 from values it loaded a step earlier). Two
+// barriers per step: one for the exchange, one for the tile buffers.
+// ---------------------------------------------------------------------------
+template <>
+__global__ __launch_bounds__(256, 2) void dkdv_kernel<128>(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
+    const float* __restrict__ lse, const float* __restrict__ delta, int S, int n,
+    const int32_t* __restrict__ q_count, const int32_t* __restrict__ q_idx,
+    const int32_t* __restrict__ order, XcdSchedule sched, float scale, float scale_log2,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+    constexpr int D = 128, KK = 8, DT = 4;
+    constexpr int TB = kBlockN * 2 * D;  // 16 KB
+    __shared__ __attribute__((aligned(1024))) char sQ0[TB];
+    __shared__ __attribute__((aligned(1024))) char sO0[TB];
+    __shared__ __attribute__((aligned(1024))) char sQ1[TB];
+    __shared__ __attribute__((aligned(1024))) char sO1[TB];
+    __shared__ __attribute__((aligned(16))) float sL0[kBlockN], sL1[kBlockN];
+    __shared__ __attribute__((aligned(16))) float sD0[kBlockN], sD1[kBlockN];
+    // The half of P (from dK waves) or dS (from dV waves) a wave hands over,
+    // [wave][group][lane]: lane-contiguous 16-byte words.
+    __shared__ __attribute__((aligned(16))) u32x4_t sX[4][2][kWave];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, c = lane & 31;
+    const int kh = wave & 1, qh = wave >> 1;  // qh 0: dV wave, 1: dK wave
+    // Workgroup-uniform (item < 2^31): the pointers derived from it stay in scalar registers.
+    const int64_t item = __builtin_amdgcn_readfirstlane((int)scheduled_item(sched, order, blockIdx.x));
+    if (item < 0) return;
+    const int64_t bh = item / n;
+    const int kb = (int)(item % n);
+    int cnt = q_count[item];
+    cnt = cnt < 0 ? 0 : (cnt > n ? n : cnt);
+    const int32_t* list = q_idx + item * (int64_t)n;
+    const int64_t head = bh * (int64_t)S * D;
+    const char* qhp = reinterpret_cast<const char*>(q + head);
+    const char* ohp = reinterpret_cast<const char*>(d_o + head);
+    const float* lh = lse + bh * (int64_t)S;
+    const float* dh = delta + bh * (int64_t)S;
+
+    const int krow = kb * kBlockN + kh * 32 + c;
+    bf16x8_t kf[KK], vf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        kf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(k + head + (int64_t)krow * D + 16 * kk + 8 * h));
+        vf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(v + head + (int64_t)krow * D + 16 * kk + 8 * h));
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        settle(kf[kk]);
+        settle(vf[kk]);
+    }
+    f32x16_t acc[DT];  // dV^T (qh = 0) or dK^T (qh = 1)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] = zero16();
+
+    // Read addresses within a tile: row 32 qh + c, chunk 2 kk + h (row reads),
+    // and the transposed reads of rows 4 h + (lane % 16) / 4 (+8), d tile t.
+    uint32_t ra[KK], ta[2][DT];
+    {
+        const int x = c & 15;
+        const int row = 32 * qh + c;
+        const uint32_t rb = (uint32_t)(row * 256 + 16 * ((h ^ (swz_k(x) & 1)) + 2 * (swz_k(x) >> 1)));
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) ra[kk] = rb ^ (32u * kk);
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+            const int xr = 8 * hi + 4 * (lane >> 5) + ((lane & 15) >> 2);
+            const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            const uint32_t tb = (uint32_t)(xr * 256 + 16 * (c0 ^ swz_k(xr)) + 8 * (lane & 1));
+#pragma unroll
+            for (int t = 0; t < DT; ++t) ta[hi][t] = tb ^ (64u * t);
+        }
+    }
+    // Direct-to-LDS loads: wave w fills row groups m = w + 4 i of both tiles.
+    uint32_t g0;
+    {
+        const int r0 = 4 * wave + (lane >> 4);
+        g0 = (uint32_t)(r0 * 256 + 16 * ((lane & 15) ^ swz_k(r0)));
+    }
+    auto entry = [&](int i) {
+        const int b = __builtin_amdgcn_readfirstlane(list[i]);
+        return (unsigned)b < (unsigned)n ? b : 0;
+    };
+    auto fetch = [&](int i, char* dq_, char* do_) {
+        const char* qs = bwd_uniform_ptr(qhp + (int64_t)i * TB);
+        const char* os = bwd_uniform_ptr(ohp + (int64_t)i * TB);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t o = g0 + 4096u * j;
+            settle(o);
+            __builtin_amdgcn_global_load_lds((bwd_gbl_void_t*)(qs + o), (bwd_lds_void_t*)(dq_ + 1024 * (wave + 4 * j)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((bwd_gbl_void_t*)(os + o), (bwd_lds_void_t*)(do_ + 1024 * (wave + 4 * j)), 16, 0, 0);
+        }
+    };
+    float rl = 0.f, rd = 0.f;  // LSE / Delta of query row `lane` of the step after next (wave 0)
+    // acc += T^T B over the query halves in order (b0: queries 0..31, b1: 32..63);
+    // slot s of B is query 32 qt + 16 u + 8 (s/4) + 4 h + s%4, matched by the
+    // transposed reads of tile T.
+    auto accumulate = [&](const char* tile, const uint32_t (&b0)[8], const uint32_t (&b1)[8]) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t* bb = qt == 0 ? b0 : b1;
+                const bf16x8_t b = as_bf16x8(make_uint4(bb[4 * u], bb[4 * u + 1], bb[4 * u + 2], bb[4 * u + 3]));
+                const char* rbp = tile + (32 * qt + 16 * u) * 256;
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(rbp + ta[0][t]));
+                    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(rbp + ta[1][t]));
+                    const uint2 ulo = __builtin_bit_cast(uint2, lo);
+                    const uint2 uhi = __builtin_bit_cast(uint2, hi);
+                    acc[t] = mfma_32x32x16(as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y)), b, acc[t]);
+                }
+            }
+    };
+    auto step = [&](int it, const char* cQ, const char* cO, const float* cL, const float* cD, char* nQ,
+                    char* nO, float* nL, float* nD) {
+        fetch(entry(min(it + 1, cnt - 1)), nQ, nO);
+        if (wave == 0) {
+            nL[lane] = rl * kLog2e;
+            nD[lane] = -rd;
+            const int i2 = entry(min(it + 2, cnt - 1));
+            rl = lh[(int64_t)i2 * kBlockN + lane];
+            rd = dh[(int64_t)i2 * kBlockN + lane];
+        }
+        uint32_t pw[8], dsw[8];
+        {
+            // S and dP quadrant: rows = queries 32 qh + c_row(r, h), column = key c.
+            // dP starts from -Delta of its rows, so the products yield dP - Delta.
+            f32x16_t sc = zero16(), dp;
+            const float* lrow = cL + 32 * qh + 4 * h;
+            const float* drow = cD + 32 * qh + 4 * h;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 d4 = *reinterpret_cast<const float4*>(drow + 8 * g);
+                dp[4 * g + 0] = d4.x;
+                dp[4 * g + 1] = d4.y;
+                dp[4 * g + 2] = d4.z;
+                dp[4 * g + 3] = d4.w;
+            }
+            {
+                bf16x8_t a[KK];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(cQ + ra[kk]));
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) sc = mfma_32x32x16(a[kk], kf[kk], sc);
+            }
+            {
+                bf16x8_t a[KK];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) a[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(cO + ra[kk]));
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) dp = mfma_32x32x16(a[kk], vf[kk], dp);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 l4 = *reinterpret_cast<const float4*>(lrow + 8 * g);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    const float p = __builtin_amdgcn_exp2f(sc[r] * scale_log2 - lv[e]);
+                    sc[r] = p;
+                    dp[r] = p * dp[r];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pw[e] = pack_bf16x2(sc[2 * e], sc[2 * e + 1]);
+                dsw[e] = pack_bf16x2(dp[2 * e], dp[2 * e + 1]);
+            }
+        }
+        // The dV wave hands over its dS and receives P, the dK wave the reverse
+        // (one code path per role, so the half handed over is dead after its write).
+        auto trade = [&](const uint32_t (&give)[8], uint32_t (&got)[8]) {
+            sX[wave][0][lane] = u32x4_t{give[0], give[1], give[2], give[3]};
+            sX[wave][1][lane] = u32x4_t{give[4], give[5], give[6], give[7]};
+            bwd_tile_barrier();
+            const u32x4_t x0 = sX[wave ^ 2][0][lane], x1 = sX[wave ^ 2][1][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                got[e] = x0[e];
+                got[4 + e] = x1[e];
+            }
+        };
+        uint32_t got[8];
+        if (qh == 0) {
+            trade(dsw, got);
+            accumulate(cO, pw, got);   // dV^T += dO^T P
+        } else {
+            trade(pw, got);
+            accumulate(cQ, got, dsw);  // dK^T += Q^T dS
+        }
+        bwd_wait_vm0();
+        bwd_tile_barrier();
+    };
+    if (cnt > 0) {
+        const int i0 = entry(0);
+        fetch(i0, sQ0, sO0);
+        if (wave == 0) {
+            sL0[lane] = lh[(int64_t)i0 * kBlockN + lane] * kLog2e;
+            sD0[lane] = -dh[(int64_t)i0 * kBlockN + lane];
+            const int i1 = entry(min(1, cnt - 1));
+            rl = lh[(int64_t)i1 * kBlockN + lane];
+            rd = dh[(int64_t)i1 * kBlockN + lane];
+        }
+        bwd_wait_vm0();
+        bwd_tile_barrier();
+        int it = 0;
+        for (; it + 1 < cnt; it += 2) {
+            step(it, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
+            step(it + 1, sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0);
+        }
+        if (it < cnt) step(it, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
+    }
+    if (qh == 0) store_t_acc<DT>(dv + head + (int64_t)krow * D, acc, 1.0f, h);
+    else store_t_acc<DT>(dk + head + (int64_t)krow * D, acc, scale, h);
+}
+
 #undef NABLA_BWD_FETCH
 #undef NABLA_BWD_STAGE
 
@@ -732,12 +1007,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
     const unsigned grid = (unsigned)sched.grid;
     const float sl2 = softmax_scale * kLog2e;
     if (D == 128)
-        dkdv_kernel<128><<<grid, 128, 0, stream>>>(
+        dkdv_kernel<128><<<grid, 256, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse,
             delta, S, n, q_count, q_idx, order, sched, softmax_scale, sl2, (uint16_t*)dk,
             (uint16_t*)dv);
     else
-        dkdv_kernel<64><<<grid, 128, 0, stream>>>(
+        dkdv_kernel<64><<<grid, 256, 0, stream>>>(
             (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse,
             delta, S, n, q_count, q_idx, order, sched, softmax_scale, sl2, (uint16_t*)dk,
             (uint16_t*)dv);

@@ -14,8 +14,11 @@
 // block is owned by one workgroup, so there are no atomics and results are
 // deterministic.
 //
-// Operand layouts follow attn_fwd.hip. Tiles are staged row-major in padded
-// LDS rows (prefetched two blocks ahead through registers). A 32 x 32
+// Operand layouts follow attn_fwd.hip. Both kernels split each (query block,
+// key block) pair into four 32 x 32 quadrants, one per wave, so two
+// workgroups -- two waves per SIMD -- share a CU. Tiles sit row-major in LDS:
+// for D = 128 moved by direct-to-LDS loads into swizzled unpadded rows (two
+// buffers), otherwise staged through registers into padded rows. A 32 x 32
 // accumulator's rows become the contraction slots of the next product's B
 // operand, and the matching A operand -- a transposed tile (K^T, dO^T, Q^T) --
 // is read with the transposing LDS read, which hands each lane one column of

@@ -351,7 +351,11 @@ def test_bwd_tiny_with_gpu_mask(thr):
     _bwd_check(q, k, v, do, lists, mask, tag=f"tiny thr={thr}", o_dtype=torch.float32)
 
 
-@pytest.mark.parametrize("B,H,n,D,p", [(1, 2, 9, 64, 0.4), (2, 1, 21, 128, 0.3), (1, 1, 1, 64, 1.0)])
+# D = 128 also with a single block, very sparse lists (empty and one-entry key lists) and dense
+# lists (long query loops of both parities), the shapes of the four-wave dK/dV kernel's branches.
+@pytest.mark.parametrize("B,H,n,D,p", [(1, 2, 9, 64, 0.4), (2, 1, 21, 128, 0.3), (1, 1, 1, 64, 1.0),
+                                       (1, 1, 1, 128, 1.0), (1, 2, 40, 128, 0.04),
+                                       (1, 1, 33, 128, 0.9)])
 def test_bwd_random_masks(B, H, n, D, p):
     q, k, v, do = _rand(B, H, 64 * n, D, seed=100 + n + D)
     mask = _random_mask(B * H, n, 200 + n, p)

@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a) {
         }
     };
 
-    // 1. row maximum; exponentials and their sum; p = e / z
+    // 1. row maximum; exponentials and their sum; p = e * (1 / z)
     const float* Lg = a.logits + row * (int64_t)n;
     float mx = -INFINITY;
     for_chunks([&](int r) {
@@ -395,7 +395,10 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a) {
         z += e;
     });
     z = wave_sum(z);
-    for_chunks([&](int r) { val(r) = val(r) / z; });
+    // One reciprocal for the row: its rounding is a factor common to every p of
+    // the row, so it cancels in the ratios the exact-order window relies on.
+    const float rz = 1.0f / z;
+    for_chunks([&](int r) { val(r) = val(r) * rz; });
 
     uint32_t tau = 0;
     bool refined = false;
@@ -522,17 +525,20 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a) {
             lo1 = tauf / g1;
             const float hi2 = tauf * g2, lo2 = tauf / g2;
             int c2 = 0;
-            unsigned long long w_up = 0;  // weight of the entries above tau e^2W
             for_chunks([&](int r) {
                 const int j = lane + 64 * r;
                 const float p = val(r);
-                const bool in2 = j < n && p >= lo2 && p <= hi2;
-                c2 += __popcll(__ballot(in2));
-                if (j < n && p > hi2) w_up += sel_weight<MODE>(p);
+                c2 += __popcll(__ballot(j < n && p >= lo2 && p <= hi2));
             });
-            w_up = wave_sum_u64(w_up);
             if (c2 >= 2) {
                 refined = true;
+                unsigned long long w_up = 0;  // weight of the entries above tau e^2W
+                for_chunks([&](int r) {
+                    const int j = lane + 64 * r;
+                    const float p = val(r);
+                    if (j < n && p > hi2) w_up += sel_weight<MODE>(p);
+                });
+                w_up = wave_sum_u64(w_up);
                 // The row in LDS so entries can be addressed by index.
                 float* prow = L.row;
                 if constexpr (!LROW) {
